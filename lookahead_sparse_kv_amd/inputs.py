@@ -1,0 +1,337 @@
+"""Seeded synthetic inputs for the Lookahead Sparse Attention hot path.
+
+The one module both sides read: it draws the tensors, and nothing else.  It
+holds no step of the scoring, gating, ranking or attention arithmetic and it
+imports neither the HIP binding nor the CPU reference.
+
+Shapes follow the workloads of the page "FlashMemory-DeepSeek-V4: Lightning
+Index Ultra-Long Context via Lookahead Sparse Attention" (gist.science),
+Technical Summary 2.1 and 4: contexts from 128K to 500K tokens stored as
+compressed entries (4 tokens per entry), HCA entries at 128:1 that are always
+kept, and selection fractions near the 13.5 % average footprint and the 10 %
+budget quoted there.  The evaluation suites the pages measure on are not used;
+only their context lengths and selection fractions are mimicked.
+
+Recipe (all draws from numpy PCG64 streams spawned from one seed):
+  * "critical" entries are contiguous runs (chunks) of keys, each key equal to
+    Gaussian noise plus alpha * u_b, where u_b is the unit mean query of
+    sequence b and alpha raises the head-mean dot product by 3 standard
+    deviations; the rest are pure noise keys;
+  * q ~ N(0, 1/d) per element (so a noise dot product is ~N(0,1)), gate
+    weights w ~ U(0,1);
+  * the indexer bias is a per-workload constant stored in
+    tests/golden/workload_bias.json (written offline from the CPU reference by
+    tests/golden/make_workload_bias.py); it is an input, like q and w;
+  * bf16 tensors are drawn in fp32 and rounded to nearest-even.
+"""
+from __future__ import annotations
+
+import json
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+BIAS_TABLE = os.path.join(_REPO, "tests", "golden", "workload_bias.json")
+
+TOKENS_PER_ENTRY = 4      # compressed KV entries: 4 tokens each
+HCA_RATIO = 128           # heavily compressed attention: 128 tokens per entry
+NOISE_PASS = 0.02         # noise entries left above the gate ("leakage")
+CLUSTER_SIGMA = 3.0       # planted keys raise the head-mean dot by 3 sigma
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    dtype: str                      # "f32" or "bf16"
+    B: int
+    T: int
+    H: int
+    D: int
+    seq_len: np.ndarray             # int32 [B]   entries per sequence (S_b)
+    key_row_start: np.ndarray       # int64 [B]   first key row of sequence b
+    entry_start: np.ndarray         # int64 [B]   offset of sequence b in per-entry outputs
+    keys: np.ndarray                # [n_key_rows, D] fp32 or uint16 (bf16 bits)
+    q: np.ndarray                   # [B, T, H, D]
+    w: np.ndarray                   # fp32 [B, T, H]
+    bias: float
+    k: int
+    Hq: int
+    Dl: int
+    qa: np.ndarray                  # [B, T, Hq, Dl]
+    latent: np.ndarray              # [n_latent_rows, Dl]
+    latent_row_start: np.ndarray    # int64 [B]
+    hca: Optional[np.ndarray]       # [n_hca_rows, Dl] or None
+    hca_row_start: Optional[np.ndarray]
+    hca_count: Optional[np.ndarray]
+    scale: float
+    planted: np.ndarray             # bool [n_key_rows]: key row belongs to a planted chunk
+    target_fraction: np.ndarray     # float [B]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def max_len(self) -> int:
+        return int(self.seq_len.max())
+
+    @property
+    def total_entries(self) -> int:
+        return int(self.entry_start[-1] + self.seq_len[-1])
+
+    @property
+    def max_hca(self) -> int:
+        return 0 if self.hca_count is None else int(self.hca_count.max())
+
+
+# name -> (description, default seed)
+CONFIGS = {
+    "tiny": "batch 1, S=1024, 4 heads x d=32 fp32, top-k 64, 8 query heads over latent 64 fp32",
+    "decode_128k": "batch 1 at 128K tokens: S=32768, 64 heads x d=128 bf16, 64 planted chunks, "
+                   "~13.5% kept, top-k 2048, 64 query heads over latent 512 bf16",
+    "decode_500k": "batch 8 at 500K tokens: S=125000, 64x128 bf16, ~10% kept, 3907 HCA rows, "
+                   "top-k 2048, 64 heads latent 512 bf16",
+    "burst_tau64": "tau=64 positions x batch 16 against one shared set of S=65536 entries, "
+                   "64x128 bf16, union over positions, top-k 2048, latent 512 bf16",
+    "ragged_mix": "batch 32, contexts 64K-512K tokens, S=len/4, 5-25% kept, HCA len/128, "
+                  "top-k 2048, latent 512 bf16",
+}
+DEFAULT_SEED = {"tiny": 11, "decode_128k": 22, "decode_500k": 33, "burst_tau64": 44,
+                "ragged_mix": 55}
+
+
+def load_bias(name: str, seed: int) -> float:
+    with open(BIAS_TABLE) as f:
+        table = json.load(f)
+    key = f"{name}:{seed}"
+    if key not in table:
+        raise KeyError(f"no stored bias for workload {key}; run tests/golden/make_workload_bias.py")
+    return float(table[key]["bias"])
+
+
+def _normal(rng, shape, std=1.0) -> np.ndarray:
+    out = rng.standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        out *= np.float32(std)
+    return out
+
+
+def _normal_bf16(rng, shape, std=1.0, chunk_rows=1 << 16) -> np.ndarray:
+    """Large N(0, std^2) bf16 tensors, drawn in row chunks to bound memory."""
+    out = np.empty(shape, dtype=np.uint16)
+    flat = out.reshape(shape[0], -1)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        flat[r0:r1] = to_bf16_bits(_normal(rng, (r1 - r0, flat.shape[1]), std))
+    return out
+
+
+def _plant(rng, keys_f32, row0, S, n_chunks, chunk_len, direction, alpha, planted):
+    """Add alpha*direction to n_chunks disjoint runs of chunk_len entries."""
+    n_slots = S // chunk_len
+    n_chunks = min(n_chunks, n_slots)
+    if n_chunks <= 0:
+        return
+    slots = rng.choice(n_slots, size=n_chunks, replace=False)
+    for sl in slots:
+        a = row0 + int(sl) * chunk_len
+        keys_f32[a:a + chunk_len] += np.float32(alpha) * direction[None, :]
+        planted[a:a + chunk_len] = True
+
+
+def _alpha_for(qh: np.ndarray, direction: np.ndarray) -> float:
+    """Scale that lifts the head-mean dot product q_h . k by CLUSTER_SIGMA
+    noise standard deviations (a noise dot has std |q_h|)."""
+    proj = qh @ direction                       # [H]
+    sigma = float(np.sqrt((qh * qh).sum(axis=1)).mean())
+    return CLUSTER_SIGMA * sigma / max(float(proj.mean()), 1e-3)
+
+
+def make_workload(name: str, seed: Optional[int] = None, bias: Optional[float] = None,
+                  with_attention: bool = True, key_replicas: int = 1) -> Workload:
+    """Draw workload `name`.  bias=None takes the stored per-workload bias."""
+    if name not in CONFIGS:
+        raise KeyError(f"unknown workload {name}; known: {sorted(CONFIGS)}")
+    seed = DEFAULT_SEED[name] if seed is None else int(seed)
+    ss = np.random.SeedSequence([seed, sorted(CONFIGS).index(name)])
+    r_shape, r_q, r_keys, r_plant, r_att, r_lat, r_hca = [np.random.Generator(np.random.PCG64(s))
+                                                          for s in ss.spawn(7)]
+    if bias is None:
+        bias = load_bias(name, seed)
+
+    if name == "tiny":
+        B, T, H, D, S = 1, 1, 4, 32, 1024
+        k, Hq, Dl = 64, 8, 64
+        seq_len = np.array([S], np.int32)
+        keys = _normal(r_keys, (S, D), 1.0 / np.sqrt(D))
+        q = _normal(r_q, (B, T, H, D))
+        w = r_q.uniform(0.0, 1.0, size=(B, T, H)).astype(np.float32)
+        qa = _normal(r_att, (B, T, Hq, Dl))
+        latent = _normal(r_lat, (S, Dl))
+        return Workload(name, seed, "f32", B, T, H, D, seq_len, np.zeros(1, np.int64),
+                        np.zeros(1, np.int64), keys, q, w, float(bias), k, Hq, Dl, qa, latent,
+                        np.zeros(1, np.int64), None, None, None, float(1.0 / np.sqrt(Dl)),
+                        np.zeros(S, bool), np.array([0.135]))
+
+    H, D, k, Hq, Dl = 64, 128, 2048, 64, 512
+    shared = False
+    hca_on = False
+    T = 1
+    if name == "decode_128k":
+        B = 1
+        seq_len = np.array([32768], np.int32)
+        frac = np.array([0.135])
+        n_chunks = np.array([64])
+    elif name == "decode_500k":
+        B = 8
+        seq_len = np.full(B, 125000, np.int32)
+        frac = np.full(B, 0.10)
+        n_chunks = np.full(B, 64)
+        hca_on = True
+    elif name == "burst_tau64":
+        B, T = 16, 64
+        seq_len = np.full(B, 65536, np.int32)
+        shared = True
+        frac = np.full(B, 0.135)
+        n_chunks = np.full(B, 8)
+    else:  # ragged_mix
+        B = 32
+        tokens = r_shape.integers(65536 // 128, 524288 // 128 + 1, size=B) * 128
+        seq_len = (tokens // TOKENS_PER_ENTRY).astype(np.int32)
+        frac = r_shape.uniform(0.05, 0.25, size=B)
+        hca_on = True
+        n_chunks = None
+
+    if shared:
+        n_key_rows = int(seq_len[0])
+        key_row_start = np.zeros(B, np.int64)
+    else:
+        n_key_rows = int(seq_len.sum())
+        key_row_start = np.concatenate([[0], np.cumsum(seq_len[:-1], dtype=np.int64)]).astype(
+            np.int64)
+    entry_start = np.concatenate([[0], np.cumsum(seq_len[:-1], dtype=np.int64)]).astype(np.int64)
+
+    # Queries: q ~ N(0, 1/d); the burst workload correlates the tau positions
+    # of one sequence around a per-sequence mean.
+    if T == 1:
+        q32 = _normal(r_q, (B, T, H, D), 1.0 / np.sqrt(D))
+    else:
+        qbar = _normal(r_q, (B, 1, H, D), 1.0 / np.sqrt(D))
+        q32 = qbar + 0.5 * _normal(r_q, (B, T, H, D), 1.0 / np.sqrt(D))
+    q = to_bf16_bits(q32)
+    qf = bf16_bits_to_f32(q)
+    w = r_q.uniform(0.0, 1.0, size=(B, T, H)).astype(np.float32)
+
+    # Keys: noise rows plus planted chunks, drawn in fp32 then rounded.
+    planted = np.zeros(n_key_rows, bool)
+    keys = np.empty((n_key_rows, D), np.uint16)
+    chunk_len = 64
+    for b in range(B):
+        qh = qf[b].mean(axis=0)                                  # [H, D] mean over positions
+        direction = qh.sum(axis=0)
+        direction /= np.linalg.norm(direction)
+        alpha = _alpha_for(qh, direction)
+        S = int(seq_len[b])
+        if shared:
+            if b == 0:
+                shared_f32 = _normal(r_keys, (S, D))
+            kf, row0 = shared_f32, 0
+        else:
+            kf, row0 = _normal(r_keys, (S, D)), 0
+        if n_chunks is not None:
+            nc = int(n_chunks[b])
+            clen = int(round(S * max(frac[b] - NOISE_PASS, 0.0) / nc)) if not shared else chunk_len
+        else:
+            clen = chunk_len
+            nc = int(round(S * max(frac[b] - NOISE_PASS, 0.0) / clen))
+        pl = planted[:S] if shared else np.zeros(S, bool)
+        _plant(r_plant, kf, row0, S, nc, max(clen, 1), direction, alpha, pl)
+        if not shared:
+            a = int(key_row_start[b])
+            keys[a:a + S] = to_bf16_bits(kf)
+            planted[a:a + S] = pl
+    if shared:
+        keys[:] = to_bf16_bits(shared_f32)
+
+    if key_replicas > 1:
+        keys = np.concatenate([keys] * key_replicas, axis=0)
+
+    if not with_attention:
+        return Workload(name, seed, "bf16", B, T, H, D, seq_len, key_row_start, entry_start, keys,
+                        q, w, float(bias), k, Hq, Dl, None, None, None, None, None, None,
+                        float(1.0 / np.sqrt(Dl)), planted, frac)
+
+    # Attention side: latent rows (one per compressed entry) and HCA rows.
+    qa = _normal_bf16(r_att, (B, T, Hq, Dl))
+    if shared:
+        latent = _normal_bf16(r_lat, (int(seq_len[0]), Dl))
+        latent_row_start = np.zeros(B, np.int64)
+    else:
+        latent = _normal_bf16(r_lat, (int(seq_len.sum()), Dl))
+        latent_row_start = key_row_start.copy()
+    hca = hca_row_start = hca_count = None
+    if hca_on:
+        tokens = seq_len.astype(np.int64) * TOKENS_PER_ENTRY
+        hca_count = ((tokens + HCA_RATIO - 1) // HCA_RATIO).astype(np.int32)
+        if name == "decode_500k":
+            # 500K tokens (decimal) -> ceil(500000 / 128) = 3907 HCA rows.
+            hca_count = np.full(B, (500000 + HCA_RATIO - 1) // HCA_RATIO, np.int32)
+        hca_row_start = np.concatenate([[0], np.cumsum(hca_count[:-1], dtype=np.int64)]).astype(
+            np.int64)
+        hca = _normal_bf16(r_hca, (int(hca_count.sum()), Dl))
+    return Workload(name, seed, "bf16", B, T, H, D, seq_len, key_row_start, entry_start, keys, q,
+                    w, float(bias), k, Hq, Dl, qa, latent, latent_row_start, hca, hca_row_start,
+                    hca_count, float(1.0 / np.sqrt(Dl)), planted, frac)
+
+
+def random_small(seed: int, B: int, T: int, H: int, D: int, lens, dtype: str = "bf16",
+                 k: int = 16, Hq: int = 16, Dl: int = 128, hca_lens=None, bias: float = 0.0,
+                 shared: bool = False, w_low: float = 0.0, int_valued: bool = False) -> Workload:
+    """Small random workload of arbitrary shape for parity sweeps and edge cases.
+
+    int_valued draws small integers (q, keys in {-2..2}, w in {0, 0.5, 1}) so
+    that every partial sum of the score is exact in fp32."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7919])))
+    lens = np.asarray(lens, np.int32)
+    assert len(lens) == B
+    if shared:
+        assert np.all(lens == lens[0])
+        n_rows = int(lens[0])
+        key_row_start = np.zeros(B, np.int64)
+    else:
+        n_rows = int(lens.sum())
+        key_row_start = np.concatenate([[0], np.cumsum(lens[:-1], dtype=np.int64)]).astype(np.int64)
+    entry_start = np.concatenate([[0], np.cumsum(lens[:-1], dtype=np.int64)]).astype(np.int64)
+    if int_valued:
+        kf = rng.integers(-2, 3, size=(n_rows, D)).astype(np.float32)
+        qf = rng.integers(-2, 3, size=(B, T, H, D)).astype(np.float32)
+        w = rng.choice(np.array([0.0, 0.5, 1.0], np.float32), size=(B, T, H))
+    else:
+        kf = _normal(rng, (n_rows, D))
+        qf = _normal(rng, (B, T, H, D), 1.0 / np.sqrt(D))
+        w = rng.uniform(w_low, 1.0, size=(B, T, H)).astype(np.float32)
+    conv = to_bf16_bits if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    qa = conv(_normal(rng, (B, T, Hq, Dl)))
+    latent = conv(_normal(rng, (n_rows, Dl)))
+    hca = hca_row_start = hca_count = None
+    if hca_lens is not None:
+        hca_count = np.asarray(hca_lens, np.int32)
+        hca_row_start = np.concatenate([[0], np.cumsum(hca_count[:-1], dtype=np.int64)]).astype(
+            np.int64)
+        hca = conv(_normal(rng, (max(int(hca_count.sum()), 1), Dl)))
+    return Workload("random_small", seed, dtype, B, T, H, D, lens, key_row_start, entry_start,
+                    conv(kf), conv(qf), w, float(bias), k, Hq, Dl, qa, latent,
+                    key_row_start.copy(), hca, hca_row_start, hca_count,
+                    float(1.0 / np.sqrt(Dl)), np.zeros(n_rows, bool), np.zeros(B))

@@ -1,0 +1,209 @@
+"""ctypes front end of the plain CPU reference (liblsa_oracle.so).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the CPU
+baseline leg of bench.py, never by the product package.  Every function
+widens its inputs exactly and computes in IEEE double precision (see
+lsa_oracle.c for the definitions and their citations).
+
+Arrays are numpy; bf16 tensors are carried as their raw uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblsa_oracle.so")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with plain gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "lsa_oracle.h"))
+    ):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    D = ctypes.c_double
+    lib.lsa_ref_index_score.argtypes = [P, I, P, P, P, I, I, I, I, P, P, D, I, P, P]
+    lib.lsa_ref_select.argtypes = [P, P, P, I, D, P, P]
+    lib.lsa_ref_topk.argtypes = [P, P, P, I, P, P, I, P, P]
+    lib.lsa_ref_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, D, P, P]
+    for f in (lib.lsa_ref_index_score, lib.lsa_ref_select, lib.lsa_ref_topk,
+              lib.lsa_ref_sparse_attend):
+        f.restype = ctypes.c_int
+    return lib
+
+
+_default_lib = None
+_lib_override = None
+
+
+def _load():
+    """The compiled reference; tests may point it at another build with use_library()."""
+    global _default_lib
+    if _lib_override is not None:
+        return _lib_override
+    if _default_lib is None:
+        build()
+        _default_lib = _bind(_LIB_PATH)
+    return _default_lib
+
+
+def use_library(path):
+    """Route every call below to the library at `path` (None restores the default).
+
+    Used by the mutation tests, which compile altered copies of lsa_oracle.c and
+    check that the pins reject them."""
+    global _lib_override
+    _lib_override = None if path is None else _bind(path)
+
+
+def compile_variant(src_text: str, out_dir: str, name: str) -> str:
+    """Compile C source text (an altered copy of lsa_oracle.c) next to the header."""
+    import shutil
+    src = os.path.join(out_dir, name + ".c")
+    with open(src, "w") as f:
+        f.write(src_text)
+    shutil.copy(os.path.join(_HERE, "lsa_oracle.h"), os.path.join(out_dir, "lsa_oracle.h"))
+    so = os.path.join(out_dir, "lib" + name + ".so")
+    subprocess.check_call(["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-w", "-o", so, src, "-lm"])
+    return so
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _dtype_code(a) -> int:
+    if a.dtype == np.float32:
+        return DTYPE_F32
+    if a.dtype == np.uint16:
+        return DTYPE_BF16
+    raise TypeError(f"oracle takes float32 or bf16 bit patterns (uint16), got {a.dtype}")
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError(f"{name}: oracle rejected the arguments (rc={rc})")
+
+
+def index_score(keys, key_row_start, seq_len, entry_start, q, w, bias, reduce_max=False,
+                want_prob=True):
+    """O1: z (and sigmoid) per (b,t,s), or the max over t when reduce_max."""
+    lib = _load()
+    keys = np.ascontiguousarray(keys)
+    q = np.ascontiguousarray(q)
+    dt = _dtype_code(keys)
+    assert _dtype_code(q) == dt, "q and keys must share a dtype"
+    B, T, H, D = q.shape
+    assert keys.shape[1] == D
+    key_row_start = _c(key_row_start, np.int64)
+    seq_len = _c(seq_len, np.int32)
+    entry_start = _c(entry_start, np.int64)
+    w = _c(w, np.float32)
+    assert w.shape == (B, T, H)
+    n_out = int(max(int(entry_start[b]) + int(seq_len[b]) for b in range(B)))
+    n_out = n_out * (1 if reduce_max else T)
+    z = np.full(n_out, np.nan, dtype=np.float64)
+    prob = np.full(n_out, np.nan, dtype=np.float64) if want_prob else None
+    rc = lib.lsa_ref_index_score(_ptr(keys), dt, _ptr(key_row_start), _ptr(seq_len),
+                                 _ptr(entry_start), B, T, H, D, _ptr(q), _ptr(w), float(bias),
+                                 1 if reduce_max else 0, _ptr(z), _ptr(prob))
+    _check(rc, "index_score")
+    return z, prob
+
+
+def select(z, entry_start, seq_len, threshold=0.0):
+    """O2: ascending candidate lists of entries with z >= threshold."""
+    lib = _load()
+    z = _c(z, np.float64)
+    entry_start = _c(entry_start, np.int64)
+    seq_len = _c(seq_len, np.int32)
+    B = len(seq_len)
+    cand_idx = np.full(len(z), -1, dtype=np.int32)
+    cand_count = np.zeros(B, dtype=np.int32)
+    rc = lib.lsa_ref_select(_ptr(z), _ptr(entry_start), _ptr(seq_len), B, float(threshold),
+                            _ptr(cand_idx), _ptr(cand_count))
+    _check(rc, "select")
+    return cand_idx, cand_count
+
+
+def topk(r, entry_start, seq_len, cand_idx, cand_count, k):
+    """O3: top-k (rank key descending, ties to the smaller index), ascending."""
+    lib = _load()
+    r = _c(r, np.float64)
+    entry_start = _c(entry_start, np.int64)
+    seq_len = _c(seq_len, np.int32)
+    cand_idx = _c(cand_idx, np.int32)
+    cand_count = _c(cand_count, np.int32)
+    B = len(seq_len)
+    topk_idx = np.full(B * k, -1, dtype=np.int32)
+    topk_count = np.zeros(B, dtype=np.int32)
+    rc = lib.lsa_ref_topk(_ptr(r), _ptr(entry_start), _ptr(seq_len), B, _ptr(cand_idx),
+                          _ptr(cand_count), int(k), _ptr(topk_idx), _ptr(topk_count))
+    _check(rc, "topk")
+    return topk_idx.reshape(B, k), topk_count
+
+
+def sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k, hca=None,
+                  hca_row_start=None, hca_count=None, scale=None):
+    """O4: attention over the top-k latent rows followed by every HCA row."""
+    lib = _load()
+    qa = np.ascontiguousarray(qa)
+    latent = np.ascontiguousarray(latent)
+    dt = _dtype_code(qa)
+    assert _dtype_code(latent) == dt
+    B, T, Hq, Dl = qa.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dl)
+    latent_row_start = _c(latent_row_start, np.int64)
+    topk_idx = _c(topk_idx, np.int32).reshape(-1)
+    topk_count = _c(topk_count, np.int32)
+    assert topk_idx.size == B * k
+    if hca is not None:
+        hca = np.ascontiguousarray(hca)
+        assert _dtype_code(hca) == dt
+        hca_row_start = _c(hca_row_start, np.int64)
+        hca_count = _c(hca_count, np.int32)
+    out = np.zeros((B, T, Hq, Dl), dtype=np.float64)
+    lse = np.zeros((B, T, Hq), dtype=np.float64)
+    rc = lib.lsa_ref_sparse_attend(_ptr(qa), dt, B, T, Hq, Dl, _ptr(latent),
+                                   _ptr(latent_row_start), _ptr(topk_idx), _ptr(topk_count),
+                                   int(k), _ptr(hca), _ptr(hca_row_start), _ptr(hca_count),
+                                   float(scale), _ptr(out), _ptr(lse))
+    _check(rc, "sparse_attend")
+    return out, lse
+
+
+def bf16_bits_to_f64(bits):
+    """Exact widening of bf16 bit patterns (uint16) to float64."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)

@@ -1,0 +1,356 @@
+"""Pins of the CPU reference against facts that do not come from the reference itself.
+
+Each test ties one reference function to a closed form, a special case that
+reduces to a library routine (numpy matmul, torch scaled-dot-product
+attention), a brute-force definition on tiny inputs, an invariant of the
+mathematics, or the hand-worked example in tests/golden.  The mutation tests
+(test_oracle_mutants.py) show that these pins reject plausible mistakes.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _score(ref, keys, q, w, bias, **kw):
+    S = keys.shape[0]
+    B = q.shape[0]
+    krs = np.zeros(B, np.int64)
+    lens = np.full(B, S, np.int32)
+    es = np.arange(B, dtype=np.int64) * S
+    return ref.index_score(keys, krs, lens, es, q, w, bias, **kw)
+
+
+# ----------------------------------------------------------------- score (O1)
+
+def test_worked_example(ref):
+    g = json.load(open(os.path.join(GOLDEN, "worked_example_score.json")))
+    keys = np.array(g["keys"], np.float32)
+    q = np.array(g["q"], np.float32)[None, None]
+    w = np.array(g["w"], np.float32)[None, None]
+    z, prob = _score(ref, keys, q, w, g["bias"])
+    assert z.tolist() == g["z"]
+    assert np.abs(prob - np.array(g["I"])).max() < 1e-15
+    cand, cnt = ref.select(z, np.zeros(1, np.int64), np.array([4], np.int32))
+    assert cand[:cnt[0]].tolist() == g["selected"]
+    t, tc = ref.topk(z, np.zeros(1, np.int64), np.array([4], np.int32), cand, cnt, g["k"])
+    assert t[0, :tc[0]].tolist() == g["topk"]
+
+
+def test_zero_weights_give_bias(ref):
+    rng = np.random.default_rng(1)
+    keys = rng.standard_normal((50, 16)).astype(np.float32)
+    q = rng.standard_normal((1, 1, 5, 16)).astype(np.float32)
+    w = np.zeros((1, 1, 5), np.float32)
+    z, prob = _score(ref, keys, q, w, -0.75)
+    assert np.all(z == -0.75)
+    assert np.allclose(prob, 1.0 / (1.0 + math.exp(0.75)), rtol=0, atol=1e-15)
+
+
+def test_negative_dots_give_bias(ref):
+    rng = np.random.default_rng(2)
+    q = np.abs(rng.standard_normal((1, 1, 6, 24))).astype(np.float32)
+    keys = -np.abs(rng.standard_normal((40, 24))).astype(np.float32)
+    w = rng.uniform(0, 1, (1, 1, 6)).astype(np.float32)
+    z, _ = _score(ref, keys, q, w, 0.25)
+    assert np.all(z == 0.25)
+
+
+def test_positive_dots_reduce_to_matmul(ref):
+    """All dots positive: the gate is inactive and the head fusion is (w^T Q) k."""
+    rng = np.random.default_rng(3)
+    q = np.abs(rng.standard_normal((1, 1, 7, 20)))
+    keys = np.abs(rng.standard_normal((33, 20)))
+    w = rng.uniform(-1, 1, (1, 1, 7))
+    z, _ = _score(ref, keys.astype(np.float32), q.astype(np.float32), w.astype(np.float32), 0.5)
+    q32, k32, w32 = (a.astype(np.float32).astype(np.float64) for a in (q, keys, w))
+    want = (w32[0, 0] @ q32[0, 0]) @ k32.T + 0.5
+    assert np.allclose(z, want, rtol=1e-12, atol=1e-12)
+
+
+def test_relu_identities_against_matmul(ref):
+    """u(q) - u(-q) = sum_h w_h x_h and u(q) + u(-q) = sum_h w_h |x_h|,
+    with x = Q k from a library matmul; together they fix u = sum_h w_h relu(x_h)."""
+    rng = np.random.default_rng(4)
+    B, T, H, D, S = 2, 3, 5, 12, 40
+    q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    keys = rng.standard_normal((S, D)).astype(np.float32)
+    w = rng.uniform(-1, 1, (B, T, H)).astype(np.float32)
+    zp, _ = _score(ref, keys, q, w, 0.0)
+    zm, _ = _score(ref, keys, -q, w, 0.0)
+    x = np.einsum("bthd,sd->bths", q.astype(np.float64), keys.astype(np.float64))
+    lin = np.einsum("bth,bths->bts", w.astype(np.float64), x).reshape(-1)
+    absd = np.einsum("bth,bths->bts", w.astype(np.float64), np.abs(x)).reshape(-1)
+    assert np.allclose(zp - zm, lin, atol=1e-10)
+    assert np.allclose(zp + zm, absd, atol=1e-10)
+
+
+def test_linear_in_weights_and_head_permutation(ref):
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 6, 16)).astype(np.float32)
+    keys = rng.standard_normal((30, 16)).astype(np.float32)
+    w1 = rng.uniform(0, 1, (1, 1, 6)).astype(np.float32)
+    w2 = rng.uniform(0, 1, (1, 1, 6)).astype(np.float32)
+    z1, _ = _score(ref, keys, q, w1, 0.0)
+    z2, _ = _score(ref, keys, q, w2, 0.0)
+    z12, _ = _score(ref, keys, q, (w1.astype(np.float64) + w2).astype(np.float32), 0.0)
+    wsum = w1.astype(np.float64) + w2
+    exact = np.all(wsum.astype(np.float32) == wsum)
+    if exact:
+        assert np.allclose(z12, z1 + z2, atol=1e-12)
+    perm = rng.permutation(6)
+    zp, _ = _score(ref, keys, q[:, :, perm], w1[:, :, perm], 0.0)
+    assert np.allclose(zp, z1, atol=1e-12)
+
+
+def test_positive_homogeneity_in_keys(ref):
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 1, 4, 8)).astype(np.float32)
+    keys = rng.standard_normal((25, 8)).astype(np.float32)
+    w = rng.uniform(0, 1, (1, 1, 4)).astype(np.float32)
+    z1, _ = _score(ref, keys, q, w, 0.0)
+    z4, _ = _score(ref, keys * np.float32(4.0), q, w, 0.0)
+    assert np.allclose(z4, 4.0 * z1, atol=1e-12)
+
+
+def test_bf16_widening_is_exact(ref):
+    """bf16 bit patterns are read as the fp32 with those upper 16 bits."""
+    from lookahead_sparse_kv_amd.inputs import to_bf16_bits
+    vals = np.array([1.0, -2.0, 0.5, 3.0, 1.5, -0.25, 0.75, 2.0], np.float32)
+    kb = to_bf16_bits(vals.reshape(1, 8))
+    qb = to_bf16_bits(np.ones((1, 1, 1, 8), np.float32))
+    z, _ = _score(ref, kb, qb, np.ones((1, 1, 1), np.float32), 0.0)
+    assert z[0] == vals.sum()
+
+
+def test_reduce_max_is_union(ref):
+    """max over positions, and the gate on the max equals the OR of per-position gates."""
+    rng = np.random.default_rng(7)
+    B, T, H, D, S = 2, 5, 3, 8, 60
+    q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+    keys = rng.standard_normal((S, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (B, T, H)).astype(np.float32)
+    z, _ = _score(ref, keys, q, w, -1.0)
+    m, pm = _score(ref, keys, q, w, -1.0, reduce_max=True)
+    zz = z.reshape(B, T, S)
+    assert np.array_equal(m.reshape(B, S), zz.max(axis=1))
+    union = (zz >= 0).any(axis=1).reshape(-1)
+    assert np.array_equal(m >= 0, union)
+    from scipy.special import expit
+    assert np.allclose(pm, expit(m), rtol=0, atol=1e-15)
+
+
+def test_sigmoid_against_library_and_gate_equivalence(ref):
+    from scipy.special import expit
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 1, 4, 8)).astype(np.float32)
+    keys = rng.standard_normal((200, 8)).astype(np.float32)
+    w = rng.uniform(0, 1, (1, 1, 4)).astype(np.float32)
+    z, prob = _score(ref, keys, q, w, -1.2)
+    assert np.allclose(prob, expit(z), rtol=0, atol=1e-15)
+    assert np.array_equal(prob >= 0.5, z >= 0)
+
+
+# ---------------------------------------------------------------- select (O2)
+
+def test_select_matches_flatnonzero_ragged(ref):
+    rng = np.random.default_rng(9)
+    lens = np.array([17, 0, 64, 5], np.int32)
+    es = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    z = rng.standard_normal(int(lens.sum()))
+    cand, cnt = ref.select(z, es, lens)
+    for b in range(4):
+        seg = z[es[b]:es[b] + lens[b]]
+        want = np.flatnonzero(seg >= 0)
+        assert cnt[b] == len(want)
+        assert np.array_equal(cand[es[b]:es[b] + cnt[b]], want)
+
+
+def test_select_boundary_values(ref):
+    z = np.array([0.0, -0.0, np.nan, -1e-300, 1e-300, np.inf, -np.inf, -5e-324])
+    cand, cnt = ref.select(z, np.zeros(1, np.int64), np.array([len(z)], np.int32))
+    assert cand[:cnt[0]].tolist() == [0, 1, 4, 5]
+
+
+def test_select_empty_and_full(ref):
+    lens = np.array([6], np.int32)
+    _, cnt = ref.select(-np.ones(6), np.zeros(1, np.int64), lens)
+    assert cnt[0] == 0
+    cand, cnt = ref.select(np.ones(6), np.zeros(1, np.int64), lens)
+    assert cnt[0] == 6 and cand.tolist() == list(range(6))
+
+
+# ------------------------------------------------------------------ top-k (O3)
+
+def _brute_topk(r, cands, k):
+    """Entry c is kept iff fewer than k candidates rank strictly ahead of it,
+    where 'ahead' = larger key, or equal key and smaller index; NaN ranks last."""
+    def ahead(a, b):  # a ahead of b
+        ra, rb = r[a], r[b]
+        na, nb = math.isnan(ra), math.isnan(rb)
+        if na != nb:
+            return nb
+        if not na and ra != rb:
+            return ra > rb
+        return a < b
+    return sorted(c for c in cands if sum(ahead(o, c) for o in cands if o != c) < k)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_brute_force_with_ties(ref, seed):
+    rng = np.random.default_rng(100 + seed)
+    S = int(rng.integers(1, 14))
+    r = rng.integers(-3, 4, size=S).astype(np.float64)        # many ties
+    if seed % 3 == 0:
+        r[rng.integers(0, S)] = np.nan
+    if seed % 4 == 1:
+        r[r == 0] = -0.0
+    cands = sorted(rng.choice(S, size=int(rng.integers(0, S + 1)), replace=False).tolist())
+    k = int(rng.integers(1, S + 2))
+    cand_idx = np.full(S, -1, np.int32)
+    cand_idx[:len(cands)] = cands
+    t, tc = ref.topk(r, np.zeros(1, np.int64), np.array([S], np.int32), cand_idx,
+                     np.array([len(cands)], np.int32), k)
+    got = t[0, :tc[0]].tolist()
+    assert got == _brute_topk(r, cands, k)
+    assert tc[0] == min(k, len(cands))
+
+
+def test_topk_invariants_ragged(ref):
+    rng = np.random.default_rng(11)
+    lens = np.array([50, 7, 0, 120], np.int32)
+    es = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    z = rng.standard_normal(int(lens.sum()))
+    cand, cnt = ref.select(z, es, lens)
+    k = 9
+    t, tc = ref.topk(z, es, lens, cand, cnt, k)
+    for b in range(len(lens)):
+        C = cand[es[b]:es[b] + cnt[b]]
+        T = t[b, :tc[b]]
+        assert tc[b] == min(k, cnt[b])
+        assert np.all(np.diff(T) > 0)
+        assert set(T.tolist()) <= set(C.tolist())
+        rest = sorted(set(C.tolist()) - set(T.tolist()))
+        if len(T) and rest:
+            seg = z[es[b]:es[b] + lens[b]]
+            assert seg[T].min() >= seg[rest].max()
+    # k >= |C| returns C itself
+    t2, tc2 = ref.topk(z, es, lens, cand, cnt, 10_000)
+    for b in range(len(lens)):
+        assert np.array_equal(t2[b, :tc2[b]], cand[es[b]:es[b] + cnt[b]])
+
+
+# -------------------------------------------------------------- attention (O4)
+
+def _sdpa(q, kv, scale):
+    """torch's scaled-dot-product attention in float64 on the CPU, K = V = kv."""
+    qt = torch.from_numpy(q)[None]             # [1, H, T, D]
+    kt = torch.from_numpy(kv)[None, None].expand(1, q.shape[0], -1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=scale)[0].numpy()
+
+
+def test_dense_special_case_matches_sdpa(ref):
+    """Every entry kept, k >= S, no HCA: sparse attention is dense attention."""
+    rng = np.random.default_rng(12)
+    B, T, Hq, Dl, S = 2, 3, 4, 16, 21
+    qa = rng.standard_normal((B, T, Hq, Dl)).astype(np.float32)
+    latent = rng.standard_normal((B * S, Dl)).astype(np.float32)
+    lrs = np.arange(B, dtype=np.int64) * S
+    k = 32
+    idx = np.full((B, k), -1, np.int32)
+    idx[:, :S] = np.arange(S)
+    out, lse = ref.sparse_attend(qa, latent, lrs, idx, np.full(B, S, np.int32), k, scale=0.3)
+    for b in range(B):
+        kv = latent[b * S:(b + 1) * S].astype(np.float64)
+        for t in range(T):
+            want = _sdpa(qa[b, t].astype(np.float64)[:, None, :], kv, 0.3)[:, 0, :]
+            assert np.allclose(out[b, t], want, atol=1e-12)
+            logits = torch.from_numpy(qa[b, t].astype(np.float64) @ kv.T * 0.3)
+            assert np.allclose(lse[b, t], torch.logsumexp(logits, dim=-1).numpy(), atol=1e-12)
+
+
+def test_hca_only_matches_sdpa_and_is_never_dropped(ref):
+    rng = np.random.default_rng(13)
+    Hq, Dl, S, NH = 3, 8, 10, 6
+    qa = rng.standard_normal((1, 1, Hq, Dl)).astype(np.float32)
+    latent = rng.standard_normal((S, Dl)).astype(np.float32)
+    hca = rng.standard_normal((NH, Dl)).astype(np.float32)
+    k = 4
+    idx = np.full((1, k), -1, np.int32)
+    out, _ = ref.sparse_attend(qa, latent, np.zeros(1, np.int64), idx, np.zeros(1, np.int32), k,
+                               hca, np.zeros(1, np.int64), np.array([NH], np.int32), 0.5)
+    want = _sdpa(qa[0, 0].astype(np.float64)[:, None, :], hca.astype(np.float64), 0.5)[:, 0, :]
+    assert np.allclose(out[0, 0], want, atol=1e-12)
+    # with top-k rows present, the HCA rows still take part
+    idx[0, :2] = [1, 7]
+    out1, _ = ref.sparse_attend(qa, latent, np.zeros(1, np.int64), idx, np.array([2], np.int32), k,
+                                hca, np.zeros(1, np.int64), np.array([NH], np.int32), 0.5)
+    kv = np.concatenate([latent[[1, 7]], hca]).astype(np.float64)
+    want1 = _sdpa(qa[0, 0].astype(np.float64)[:, None, :], kv, 0.5)[:, 0, :]
+    assert np.allclose(out1[0, 0], want1, atol=1e-12)
+    for i in range(NH):
+        h2 = hca.copy()
+        h2[i] += 1.0
+        out2, _ = ref.sparse_attend(qa, latent, np.zeros(1, np.int64), idx, np.array([2], np.int32),
+                                    k, h2, np.zeros(1, np.int64), np.array([NH], np.int32), 0.5)
+        assert not np.allclose(out2, out1)
+
+
+def test_single_row_equal_logits_and_empty(ref):
+    rng = np.random.default_rng(14)
+    Dl = 8
+    latent = rng.standard_normal((5, Dl)).astype(np.float32)
+    qa = rng.standard_normal((1, 1, 2, Dl)).astype(np.float32)
+    idx = np.array([[3, -1, -1]], np.int32)
+    out, lse = ref.sparse_attend(qa, latent, np.zeros(1, np.int64), idx, np.array([1], np.int32), 3,
+                                 scale=0.7)
+    assert np.array_equal(out[0, 0], np.tile(latent[3].astype(np.float64), (2, 1)))
+    assert np.allclose(lse[0, 0], 0.7 * qa[0, 0].astype(np.float64) @ latent[3], atol=1e-13)
+    # equal logits: zero query -> mean of the rows, lse = log(n)
+    idx = np.array([[0, 2, 4]], np.int32)
+    out, lse = ref.sparse_attend(np.zeros_like(qa), latent, np.zeros(1, np.int64), idx,
+                                 np.array([3], np.int32), 3)
+    assert np.allclose(out[0, 0], latent[[0, 2, 4]].astype(np.float64).mean(0), atol=1e-15)
+    assert np.allclose(lse, math.log(3), atol=1e-15)
+    # nothing to attend
+    out, lse = ref.sparse_attend(qa, latent, np.zeros(1, np.int64), idx, np.array([0], np.int32), 3)
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_pipeline_all_selected_is_dense(ref):
+    """Gate passes everything, k >= S, no HCA: score->select->top-k->attend is dense attention."""
+    rng = np.random.default_rng(15)
+    S, H, D, Hq, Dl = 30, 4, 8, 2, 16
+    keys = rng.standard_normal((S, D)).astype(np.float32)
+    q = rng.standard_normal((1, 1, H, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (1, 1, H)).astype(np.float32)
+    z, _ = _score(ref, keys, q, w, 100.0)
+    lens = np.array([S], np.int32)
+    es = np.zeros(1, np.int64)
+    cand, cnt = ref.select(z, es, lens)
+    assert cnt[0] == S
+    t, tc = ref.topk(z, es, lens, cand, cnt, 64)
+    latent = rng.standard_normal((S, Dl)).astype(np.float32)
+    qa = rng.standard_normal((1, 1, Hq, Dl)).astype(np.float32)
+    out, _ = ref.sparse_attend(qa, latent, es, t, tc, 64, scale=0.25)
+    want = _sdpa(qa[0, 0].astype(np.float64)[:, None, :], latent.astype(np.float64), 0.25)[:, 0, :]
+    assert np.allclose(out[0, 0], want, atol=1e-12)
+
+
+def test_topk_nan_ranks_last_and_signed_zero_ties(ref):
+    r = np.array([1.0, np.nan, 3.0, 2.0, -0.0, 0.0, np.nan])
+    S = len(r)
+    lens = np.array([S], np.int32)
+    es = np.zeros(1, np.int64)
+    cand = np.arange(S, dtype=np.int32)
+    cnt = np.array([S], np.int32)
+    want = {1: [2], 2: [2, 3], 3: [0, 2, 3], 4: [0, 2, 3, 4], 5: [0, 2, 3, 4, 5],
+            6: [0, 1, 2, 3, 4, 5], 7: list(range(7))}
+    for k, w in want.items():
+        t, tc = ref.topk(r, es, lens, cand, cnt, k)
+        assert t[0, :tc[0]].tolist() == w, k
