@@ -1,0 +1,250 @@
+"""Benchmark of the LSA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: index score (max over
+positions) -> gate + compaction -> top-k -> sparse attention, all enqueued on
+one stream.  The default workload is 8 sequences at 500K tokens (125000
+compressed entries each, 3907 HCA rows, top-k 2048, latent 512, 64 heads).
+
+Prints one JSON line.  `value` = indexer scores per second of whole steps
+(sum of S_b per step / step time).  The roofline object covers the score
+kernel, the dominant one by bytes; the attention kernel gets a second one.
+Inputs are resident in HBM before timing; key and latent pools are replicated
+and rotated so each timed launch reads memory the 256 MB on-die cache does
+not hold.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+REPO = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, REPO)
+
+METRIC = "indexer scores/sec + sparse-attn decode tokens/sec at 500K ctx; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix, TFLOP/s
+ROTATE_BYTES = 1 << 30         # distinct bytes per rotation cycle (>= 4x the on-die cache)
+PROFILES = os.path.join(REPO, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode_500k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences the CPU baseline scores")
+    ap.add_argument("--kernel-reps", type=int, default=0,
+                    help="launches per timing interval (0 = pick for >= 1 ms)")
+    ap.add_argument("--profile-launches", type=int, default=0,
+                    help="only run N launches of each kernel (for rocprofv3 counter runs)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="with --profile-launches: also run a plain copy of this many bytes")
+    return ap.parse_args()
+
+
+def src_sha(name: str) -> str:
+    p = os.path.join(REPO, "lookahead_sparse_kv_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str, src: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if still valid for this source."""
+    path = os.path.join(PROFILES, f"{kernel}.{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_sha") != src_sha(src):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def timed(torch, stream, fn, reps, intervals=7, warm=2):
+    """Median per-launch time (s) of `fn(i)` over `intervals` runs of `reps` launches,
+    measured with HIP events recorded on `stream` (the stream the kernels run on)."""
+    res = []
+    i = 0
+    for it in range(warm + intervals):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn(i)
+            i += 1
+        e1.record(stream)
+        e1.synchronize()
+        if it >= warm:
+            res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+    return statistics.median(res)
+
+
+def cpu_baseline(wl, nseq: int):
+    """The CPU reference as it stands (single thread) on sequences 0..nseq-1 of the workload:
+    score, gate, top-k and attention of those sequences; returned as scores/s."""
+    from oracle import oracle
+    oracle.build()
+    nseq = min(nseq, wl.B)
+    t0 = time.perf_counter()
+    for b in range(nseq):
+        S = int(wl.seq_len[b])
+        kr = int(wl.key_row_start[b])
+        z, _ = oracle.index_score(wl.keys[kr:kr + S], np.zeros(1, np.int64), wl.seq_len[b:b + 1],
+                                  np.zeros(1, np.int64), wl.q[b:b + 1], wl.w[b:b + 1], wl.bias,
+                                  reduce_max=True, want_prob=False)
+        c, n = oracle.select(z, np.zeros(1, np.int64), wl.seq_len[b:b + 1])
+        t, tn = oracle.topk(z, np.zeros(1, np.int64), wl.seq_len[b:b + 1], c, n, wl.k)
+        oracle.sparse_attend(wl.qa[b:b + 1], wl.latent, wl.latent_row_start[b:b + 1], t, tn, wl.k,
+                             wl.hca, None if wl.hca is None else wl.hca_row_start[b:b + 1],
+                             None if wl.hca is None else wl.hca_count[b:b + 1], wl.scale)
+    dt = time.perf_counter() - t0
+    scores = int(wl.seq_len[:nseq].sum()) * wl.T
+    return {"value": scores / dt, "unit": "scores/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole path (score, gate, top-k, attention) of sequences 0..{nseq - 1} of "
+                      f"{wl.B}, {scores} scores, {dt:.1f} s single-threaded",
+            "decode_tokens_per_s": nseq * wl.T / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by "
+              f"sequence with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from lookahead_sparse_kv_amd import binding as lsa
+    from lookahead_sparse_kv_amd import inputs
+    from lookahead_sparse_kv_amd.pipeline import DeviceInputs, Pipeline
+
+    lsa.load_library()
+    t_gen = time.time()
+    wl = inputs.make_workload(args.workload)
+    key_bytes = wl.keys.nbytes
+    rk = max(1, -(-ROTATE_BYTES // key_bytes))
+    # bytes the attention touches per launch (top-k rows + HCA rows)
+    att_rows = wl.B * (wl.k + wl.max_hca)
+    att_bytes = att_rows * wl.Dl * 2
+    rl = max(1, -(-ROTATE_BYTES // att_bytes))
+    if args.profile_launches:
+        rk, rl = 1, 1
+    stream = torch.cuda.Stream()   # default priority
+    with torch.cuda.stream(stream):
+        d = DeviceInputs(wl, key_replicas=rk, latent_replicas=rl)
+        p = Pipeline(d)
+    torch.cuda.synchronize()
+    print(f"[bench] workload {args.workload} ready in {time.time() - t_gen:.1f}s; key replicas "
+          f"{rk}, latent replicas {rl}", file=sys.stderr, flush=True)
+
+    with torch.cuda.stream(stream):
+        if args.profile_launches:
+            for i in range(args.profile_launches):
+                p.step(i)
+            if args.copy_bytes:
+                a = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+                b = torch.empty_like(a)
+                for _ in range(args.profile_launches):
+                    b.copy_(a)
+            torch.cuda.synchronize()
+            print(json.dumps({"profile_launches": args.profile_launches,
+                              "copy_bytes": args.copy_bytes}))
+            return
+
+        for i in range(args.warmup):
+            p.step(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            p.step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+
+        # per-kernel launch durations (same stream, HIP events), rotating replicas
+        def reps_for(est_s):
+            return args.kernel_reps or max(5, int(1e-3 / max(est_s, 1e-7)) + 1)
+        t_score = timed(torch, stream, lambda i: p.score(i), reps_for(step_s / 2))
+        t_select = timed(torch, stream, lambda i: p.select(), reps_for(1e-5))
+        t_topk = timed(torch, stream, lambda i: p.topk(), reps_for(2e-5))
+        t_attend = timed(torch, stream, lambda i: p.attend(i), reps_for(step_s / 4))
+
+    torch.cuda.synchronize()
+    counts = p.cand_count.cpu().numpy()
+    scores_per_step = int(wl.seq_len.sum()) * wl.T
+    # algorithmic bytes of one score launch: every key once, the queries and gates, the logits
+    if wl.B > 1 and int(wl.key_row_start.max()) == 0:
+        score_bytes = int(wl.seq_len[0]) * wl.D * 2          # one key set shared by the batch
+    else:
+        score_bytes = int(wl.seq_len.sum()) * wl.D * 2
+    score_bytes += wl.q.nbytes + wl.w.nbytes + int(wl.seq_len.sum()) * 4
+    score_flops = 2.0 * scores_per_step * wl.H * wl.D
+    att_alg_bytes = att_bytes + wl.qa.nbytes * 2 + wl.B * wl.k * 4   # rows, qa in, out, indices
+    att_flops = 4.0 * wl.B * wl.T * wl.Hq * (wl.k + wl.max_hca) * wl.Dl
+
+    def roof(bound, alg, t, peak, unit, traffic):
+        ach = alg / t / (1e9 if unit == "GB/s" else 1e12)
+        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+                "frac": round(ach / peak, 4), "traffic": traffic}
+
+    if wl.T == 1:
+        roofline = roof("hbm", score_bytes, t_score, HBM_PEAK_GBS, "GB/s",
+                        read_traffic("score_decode", args.workload, "score.hip"))
+    else:
+        roofline = roof("mfma", score_flops, t_score, BF16_PEAK_TFLOPS, "TFLOP/s", None)
+    roof_att = roof("hbm", att_alg_bytes, t_attend, HBM_PEAK_GBS, "GB/s",
+                    read_traffic("attend", args.workload, "attend.hip"))
+    roof_att["mfma_frac"] = round(att_flops / t_attend / 1e12 / BF16_PEAK_TFLOPS, 4)
+
+    line = {
+        "metric": METRIC,
+        "value": round(scores_per_step / step_s, 1),
+        "unit": "scores/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; planted critical chunks among Gaussian noise keys)",
+        "config": {"workload": args.workload, "batch": wl.B, "positions": wl.T,
+                   "entries_per_seq": int(wl.seq_len.max()), "indexer_heads": wl.H,
+                   "d_idx": wl.D, "topk": wl.k, "query_heads": wl.Hq, "latent_dim": wl.Dl,
+                   "hca_rows_per_seq": wl.max_hca, "parallelism": "single GPU"},
+        "kernels_us": {"index_score": round(t_score * 1e6, 2),
+                       "select_compact": round(t_select * 1e6, 2),
+                       "topk": round(t_topk * 1e6, 2),
+                       "sparse_attend": round(t_attend * 1e6, 2)},
+        "index_scores_per_s": round(scores_per_step / t_score, 1),
+        "decode_tokens_per_s": round(wl.B * wl.T / t_attend, 1),
+        "decode_tokens_per_s_tau64": round(
+            wl.B * wl.T / (t_attend + (t_score + t_select + t_topk) / 64.0), 1),
+        "selected_fraction": round(float(counts.sum()) / float(wl.seq_len.sum()), 4),
+        "roofline": roofline,
+        "roofline_attend": roof_att,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seqs)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

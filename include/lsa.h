@@ -1,0 +1,169 @@
+/*
+ * lsa.h -- C ABI of the Lookahead Sparse Attention (LSA) hot path on MI355X (gfx950).
+ *
+ * The four calls follow the decode path described on the page
+ * "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via Lookahead
+ * Sparse Attention" (gist.science/paper/2606.09079), Technical Summary
+ * section 2.1 "Architectural Design":
+ *   lsa_index_score     -- the Memory Indexer's lookahead index score I_{t,s}
+ *                          against every preceding compressed entry ("Scoring
+ *                          Mechanism"), with the OR-union over positions of
+ *                          section 2.4 "Optimal Configuration";
+ *   lsa_select_compact  -- keep every entry whose score reaches 0.5 ("Dynamic
+ *                          Fetching"), as an ascending index list;
+ *   lsa_topk            -- fine-grained top-k inside that subset ("Tiered
+ *                          Selection");
+ *   lsa_sparse_attend   -- the final core attention over the chosen entries
+ *                          plus every heavily compressed (HCA, 128:1) entry,
+ *                          which the design always keeps (opening paragraph of
+ *                          section 2.1).
+ * The output of each call is an input of the next.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers are DEVICE pointers unless stated otherwise.  `stream` is a
+ *   hipStream_t passed as void* (NULL = the null stream).  All work is
+ *   enqueued asynchronously on `stream`; the library never synchronises.
+ * - The caller owns every buffer, including the workspace (size it with
+ *   lsa_workspace_bytes).  The library allocates and frees no device memory
+ *   and keeps no pointer after a call returns.
+ * - Ragged batches: sequence b (0 <= b < B) owns S_b = seq_len[b] compressed
+ *   entries.  Its key rows are pool rows key_row_start[b] .. +S_b-1 (a start
+ *   of 0 for every b shares one key set across the batch).  Per-entry outputs
+ *   of sequence b (scores, candidate lists) live at element entry_start[b]
+ *   of their arrays, so entry_start is normally the exclusive prefix sum of
+ *   seq_len.  Entry indices s in index lists are relative to the sequence
+ *   (0 <= s < S_b).
+ * - max_len (host) must be >= every seq_len[b]; it sizes the grids without a
+ *   device-to-host copy.  Device index arrays must satisfy the stated
+ *   bounds; they are not checked on the host (that would need a sync).
+ * - Row pools (keys, latent rows, HCA rows) are row-major with contiguous
+ *   rows; base pointers and q/qa must be 16-byte aligned.
+ * - Return value: LSA_OK, or a negative status.  Arguments are validated on
+ *   the host before anything is enqueued; on error nothing is enqueued, no
+ *   output is touched, and lsa_last_error() describes the problem.  Faults
+ *   inside kernels surface at the caller's next synchronisation.
+ * - Calls are reentrant and hold no global mutable state besides a
+ *   thread-local error message and a per-device cache of the device's
+ *   properties.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_OK 0
+#define LSA_ERR_INVALID_ARG (-1)  /* null pointer, bad size, misalignment, bad dtype  */
+#define LSA_ERR_UNSUPPORTED (-2)  /* shape outside the kernels' envelope, not gfx950  */
+#define LSA_ERR_WORKSPACE (-3)    /* workspace missing or smaller than required       */
+#define LSA_ERR_HIP (-4)          /* the HIP runtime reported an error at launch      */
+
+#define LSA_DTYPE_F32 0
+#define LSA_DTYPE_BF16 1
+
+#define LSA_OP_SELECT 1
+#define LSA_OP_TOPK 2
+#define LSA_OP_ATTEND 3
+
+/* Lookahead index score (section 2.1 "Scoring Mechanism"; the query/key
+ * interaction is a dot product per section 5 "Architectural Constraints").
+ * This library's instance of the head-fused gated score:
+ *     z[b,t,s] = sum_h w[b,t,h] * max(0, <q[b,t,h,:], k[b,s,:]>) + bias,
+ *     I[b,t,s] = sigmoid(z[b,t,s]).
+ *   keys   [rows, D] in `dtype` (LSA_DTYPE_BF16 or LSA_DTYPE_F32)
+ *   q      [B, T, H, D], same dtype as keys
+ *   w      [B, T, H] fp32 (any sign)
+ *   bias   host fp32 scalar
+ *   reduce_max = 0: z_out (and prob_out) hold, for sequence b, a [T, S_b]
+ *                   block starting at element entry_start[b] * T.
+ *   reduce_max = 1: z_out holds m[b,s] = max_t z[b,t,s] at element
+ *                   entry_start[b] + s -- the OR-union of the per-position
+ *                   gates of section 2.4 is exactly the gate on m;
+ *                   prob_out, if given, holds sigmoid(m).
+ *   prob_out may be NULL.  Accumulation is fp32; bf16 products are exact.
+ * Envelope: B, T, H, D >= 1; the bf16 matrix-core path takes H <= 64 and
+ * D in {64, 128}; other shapes (and fp32) use the vector path, which needs
+ * T*H*(D+1) <= 16384.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
+                    const int32_t* seq_len, const int64_t* entry_start, int B, int T, int H,
+                    int D, int64_t max_len, const void* q, const float* w, float bias,
+                    int reduce_max, float* z_out, float* prob_out, void* stream);
+
+/* Dynamic fetching (section 2.1): keep every entry with I >= 0.5, with no
+ * fixed count.  I >= 0.5 holds exactly when z >= 0, so the gate is taken on
+ * the fp32 logit: candidate s of sequence b iff z[entry_start[b]+s] >=
+ * threshold (pass 0.0f for the 0.5 gate; -0.0 passes, NaN never does).
+ *   cand_idx   int32, the ascending list of kept s for sequence b written at
+ *              cand_idx[entry_start[b] ...]; capacity S_b per sequence.
+ *   cand_count int32 [B].
+ *   workspace  lsa_workspace_bytes(LSA_OP_SELECT, B, 0, 0, 0, max_len, 0, 0) bytes.
+ * Deterministic: the list is in ascending s whatever the launch order.
+ * Errors: INVALID_ARG, WORKSPACE, HIP. */
+int lsa_select_compact(const float* z, const int64_t* entry_start, const int32_t* seq_len,
+                       int B, int64_t max_len, float threshold, int32_t* cand_idx,
+                       int32_t* cand_count, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Tiered selection (section 2.1): the top-k candidates of each sequence by
+ * rank key r[entry_start[b] + s] (fp32; the pipeline passes the indexer logit
+ * or its max over positions).  Order: larger key first, equal keys by smaller
+ * s, NaN after every number, -0.0 equal to +0.0.
+ *   cand_idx/cand_count as written by lsa_select_compact (cand_count[b] <= S_b).
+ *   topk_idx   int32 [B, k]: the kept s of sequence b in ascending order in
+ *              row b; entries past topk_count[b] are left untouched.
+ *   topk_count int32 [B] = min(k, cand_count[b]).
+ *   workspace  lsa_workspace_bytes(LSA_OP_TOPK, B, 0, 0, 0, max_len, k, 0) bytes.
+ * Envelope: 1 <= k <= 65536.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int lsa_topk(const float* rank_key, const int64_t* entry_start, const int32_t* seq_len, int B,
+             int64_t max_len, const int32_t* cand_idx, const int32_t* cand_count, int k,
+             int32_t* topk_idx, int32_t* topk_count, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Core attention over the chosen entries plus all HCA entries (section 2.1).
+ * One latent row per compressed entry serves as both key and value for all
+ * Hq query heads.  For each (b, t, h) the attended rows are
+ *     latent rows latent_row_start[b] + topk_idx[b*k + j], j < topk_count[b],
+ *     then HCA rows hca_row_start[b] + i, i < hca_count[b];
+ * logit_j = scale * <qa[b,t,h,:], row_j>,
+ * out[b,t,h,:] = sum_j softmax(logit)_j * row_j,  lse[b,t,h] = logsumexp(logit).
+ * Rows with no attended entry give out = 0 and lse = -inf.
+ *   qa  [B, T, Hq, Dl] in `dtype`; latent and hca rows of Dl elements, same dtype.
+ *   hca may be NULL (then hca_row_start/hca_count are ignored); otherwise
+ *   hca_count[b] <= max_hca (host).
+ *   out [B, T, Hq, Dl] in `dtype`; lse [B, T, Hq] fp32 or NULL.
+ *   workspace  lsa_workspace_bytes(LSA_OP_ATTEND, B, T, Hq, Dl, 0, k, max_hca)
+ *              bytes (split partial results); may be 0 for some shapes.
+ * Envelope: the bf16 matrix-core path takes Hq <= 64 and Dl in {128, 256,
+ * 512}; other shapes (and fp32) use the vector path (Dl <= 1024).
+ * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
+int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int Dl,
+                      const void* latent, const int64_t* latent_row_start,
+                      const int32_t* topk_idx, const int32_t* topk_count, int k,
+                      const void* hca, const int64_t* hca_row_start, const int32_t* hca_count,
+                      int64_t max_hca, float scale, void* out, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* Workspace bytes needed by op (LSA_OP_*) for the given host-side sizes;
+ * arguments an op does not use are ignored.  Returns 0 for an unknown op. */
+size_t lsa_workspace_bytes(int op, int B, int T, int Hq, int Dl, int64_t max_len, int k,
+                           int64_t max_hca);
+
+/* Static description of a status code. */
+const char* lsa_status_string(int status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* lsa_last_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int lsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H */

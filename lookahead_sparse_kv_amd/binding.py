@@ -1,0 +1,189 @@
+"""ctypes binding of liblsa.so: same names as the C entry points, torch tensors in.
+
+Argument marshalling only: every step runs in the HIP kernels of liblsa.so.
+Tensors must live on the current HIP device; work is enqueued on the current
+torch stream unless `stream` (a torch.cuda.Stream) is given.  There is no
+fallback: if the library is missing the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblsa.so")
+
+LSA_OK = 0
+LSA_ERR_INVALID_ARG = -1
+LSA_ERR_UNSUPPORTED = -2
+LSA_ERR_WORKSPACE = -3
+LSA_ERR_HIP = -4
+LSA_DTYPE_F32 = 0
+LSA_DTYPE_BF16 = 1
+LSA_OP_SELECT = 1
+LSA_OP_TOPK = 2
+LSA_OP_ATTEND = 3
+
+EXPORTED = ["lsa_index_score", "lsa_select_compact", "lsa_topk", "lsa_sparse_attend",
+            "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
+
+
+class LSAError(RuntimeError):
+    def __init__(self, call: str, status: int, detail: str):
+        super().__init__(f"{call} failed with status {status}: {detail}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load liblsa.so (built by lookahead_sparse_kv_amd.build); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m lookahead_sparse_kv_amd.build`"
+                           " (the HIP library has no fallback)")
+    lib = ctypes.CDLL(path)
+    P, I, L, F, Z = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                     ctypes.c_size_t)
+    lib.lsa_index_score.argtypes = [P, I, P, P, P, I, I, I, I, L, P, P, F, I, P, P, P]
+    lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
+    lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, P, Z, P]
+    lib.lsa_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, L, F, P, P, P, Z, P]
+    lib.lsa_workspace_bytes.argtypes = [I, I, I, I, I, L, I, L]
+    lib.lsa_workspace_bytes.restype = Z
+    lib.lsa_status_string.argtypes = [I]
+    lib.lsa_status_string.restype = ctypes.c_char_p
+    lib.lsa_last_error.argtypes = []
+    lib.lsa_last_error.restype = ctypes.c_char_p
+    lib.lsa_version.argtypes = []
+    lib.lsa_version.restype = I
+    for name in ("lsa_index_score", "lsa_select_compact", "lsa_topk", "lsa_sparse_attend"):
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def _check(call: str, rc: int):
+    if rc != LSA_OK:
+        lib = load_library()
+        raise LSAError(call, rc, lib.lsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return LSA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return LSA_DTYPE_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def lsa_workspace_bytes(op: int, B: int, T: int = 0, Hq: int = 0, Dl: int = 0, max_len: int = 0,
+                        k: int = 0, max_hca: int = 0) -> int:
+    return int(load_library().lsa_workspace_bytes(op, B, T, Hq, Dl, max_len, k, max_hca))
+
+
+def lsa_version() -> int:
+    return int(load_library().lsa_version())
+
+
+def lsa_index_score(keys, key_row_start, seq_len, entry_start, max_len: int, q, w, bias: float,
+                    reduce_max: bool = False, z_out=None, prob_out=None, stream=None):
+    """Score every entry (see include/lsa.h).  q: [B, T, H, D], w: [B, T, H]."""
+    lib = load_library()
+    B, T, H, D = q.shape
+    _dev(keys, "keys")
+    _dev(q, "q", keys.dtype)
+    _dev(w, "w", torch.float32)
+    _dev(key_row_start, "key_row_start", torch.int64)
+    _dev(seq_len, "seq_len", torch.int32)
+    _dev(entry_start, "entry_start", torch.int64)
+    if z_out is None:
+        raise ValueError("z_out must be preallocated (its size depends on entry_start)")
+    _dev(z_out, "z_out", torch.float32)
+    if prob_out is not None:
+        _dev(prob_out, "prob_out", torch.float32)
+    rc = lib.lsa_index_score(_ptr(keys), _dtype_code(keys), _ptr(key_row_start), _ptr(seq_len),
+                             _ptr(entry_start), B, T, H, D, int(max_len), _ptr(q), _ptr(w),
+                             float(bias), 1 if reduce_max else 0, _ptr(z_out), _ptr(prob_out),
+                             _stream(stream))
+    _check("lsa_index_score", rc)
+    return z_out, prob_out
+
+
+def lsa_select_compact(z, entry_start, seq_len, max_len: int, cand_idx, cand_count, workspace,
+                       threshold: float = 0.0, stream=None):
+    lib = load_library()
+    _dev(z, "z", torch.float32)
+    _dev(cand_idx, "cand_idx", torch.int32)
+    _dev(cand_count, "cand_count", torch.int32)
+    B = seq_len.numel()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.lsa_select_compact(_ptr(z), _ptr(entry_start), _ptr(seq_len), B, int(max_len),
+                                float(threshold), _ptr(cand_idx), _ptr(cand_count),
+                                _ptr(workspace), ws_bytes, _stream(stream))
+    _check("lsa_select_compact", rc)
+    return cand_idx, cand_count
+
+
+def lsa_topk(rank_key, entry_start, seq_len, max_len: int, cand_idx, cand_count, k: int,
+             topk_idx, topk_count, workspace=None, stream=None):
+    lib = load_library()
+    _dev(rank_key, "rank_key", torch.float32)
+    _dev(topk_idx, "topk_idx", torch.int32)
+    _dev(topk_count, "topk_count", torch.int32)
+    B = seq_len.numel()
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.lsa_topk(_ptr(rank_key), _ptr(entry_start), _ptr(seq_len), B, int(max_len),
+                      _ptr(cand_idx), _ptr(cand_count), int(k), _ptr(topk_idx), _ptr(topk_count),
+                      _ptr(workspace), ws_bytes, _stream(stream))
+    _check("lsa_topk", rc)
+    return topk_idx, topk_count
+
+
+def lsa_sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k: int, out,
+                      hca=None, hca_row_start=None, hca_count=None, max_hca: int = 0,
+                      scale: Optional[float] = None, lse=None, workspace=None, stream=None):
+    lib = load_library()
+    B, T, Hq, Dl = qa.shape
+    _dev(qa, "qa")
+    _dev(latent, "latent", qa.dtype)
+    _dev(out, "out", qa.dtype)
+    if hca is not None:
+        _dev(hca, "hca", qa.dtype)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32)
+    if scale is None:
+        scale = Dl ** -0.5
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.lsa_sparse_attend(_ptr(qa), _dtype_code(qa), B, T, Hq, Dl, _ptr(latent),
+                               _ptr(latent_row_start), _ptr(topk_idx), _ptr(topk_count), int(k),
+                               _ptr(hca), _ptr(hca_row_start), _ptr(hca_count), int(max_hca),
+                               float(scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                               _stream(stream))
+    _check("lsa_sparse_attend", rc)
+    return out, lse

@@ -1,0 +1,373 @@
+// score.hip -- lsa_index_score: the Memory Indexer's lookahead index score.
+//
+// Definition (page "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context
+// via Lookahead Sparse Attention", Technical Summary 2.1 "Scoring Mechanism";
+// dot-product interaction per section 5): a head-fused, gated score
+//     z[b,t,s] = sum_h w[b,t,h] * max(0, <q[b,t,h,:], k[b,s,:]>) + bias
+// and I = sigmoid(z).  With T query positions per sequence the OR-union of
+// per-position gates (section 2.4) is the gate on max_t z.
+//
+// Three kernels:
+//  * score_decode (T = 1, bf16): streams each key row once from HBM.  All H
+//    heads share the key, so one 256-byte key feeds 64 x 128 multiply-adds:
+//    ~63 flop/byte, above the fp32 vector ridge (~20 flop/byte) and below the
+//    bf16 matrix ridge, hence the matrix cores run over the head dimension
+//    (M = heads, N = 16 entries, K = d) and HBM stays the bound.
+//  * score_burst (T > 1, bf16): a dense contraction of T*H query rows against
+//    the keys (matrix-core bound); the ReLU, the weighted head sum and the
+//    max over positions are fused into the epilogue.
+//  * score_vector: any shape, fp32 or bf16, plain vector arithmetic (small
+//    shapes, tests).
+#include "common.hpp"
+
+namespace lsa {
+
+// ----------------------------------------------------------------- decode
+// One wave scores groups of 16 consecutive entries of one sequence.
+//   lane l: n = l%16 selects the entry, g = l/16 selects 8 of each 32 dims.
+//   A (queries) stays in registers for the whole wave: MT x KT operands.
+//   B (keys): for k-step kk the lane loads dims 32kk + 8g .. +7 of its entry,
+//   so one load instruction reads 64 contiguous bytes of 16 key rows.
+//   D[4g+v][n] of head tile mt is head 16mt + 4g + v of entry n.
+template <int MT, int KT>
+__global__ __launch_bounds__(256) void k_score_decode(
+    const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
+    const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int H,
+    int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
+    float* __restrict__ z_out, float* __restrict__ prob_out, int groups_per_wave) {
+    constexpr int D = 32 * KT;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t S = min((int64_t)seq_len[b], max_len);
+    const int64_t first = ((int64_t)blockIdx.x * 4 + wave) * (int64_t)groups_per_wave * 16;
+    if (first >= S) return;
+    const int64_t last = min(first + (int64_t)groups_per_wave * 16, S);
+    const int n16 = lane & 15;
+    const int g = lane >> 4;
+
+    bf16x8 qa[MT][KT];
+    float wv[MT][4];
+    const bf16* qb = q + (int64_t)b * H * D;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int head = 16 * mt + n16;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk)
+            qa[mt][kk] = head < H ? load8(qb + (int64_t)head * D + 32 * kk + 8 * g) : zero8();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int hv = 16 * mt + 4 * g + v;
+            wv[mt][v] = hv < H ? w[(int64_t)b * H + hv] : 0.0f;
+        }
+    }
+
+    const bf16* kbase = keys + key_row_start[b] * D + 8 * g;
+    const int64_t eo = entry_start[b];
+
+    auto load_group = [&](int64_t e0, bf16x8 (&kb)[KT]) {
+        const int64_t n = e0 + n16;
+        const int64_t row = n < last ? n : e0;  // e0 < last always
+        const bf16* p = kbase + row * D;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) kb[kk] = load8(p + 32 * kk);
+    };
+    auto score_group = [&](int64_t e0, const bf16x8 (&kb)[KT]) {
+        f32x4 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(qa[mt][kk], kb[kk], acc[mt]);
+        float s = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
+        s += __shfl_xor(s, 16);
+        s += __shfl_xor(s, 32);
+        const int64_t n = e0 + n16;
+        if (g == 0 && n < last) {
+            const float z = s + bias;
+            z_out[eo + n] = z;
+            if (prob_out) prob_out[eo + n] = sigmoidf(z);
+        }
+    };
+
+    // Two groups in flight per wave: prefetch the next group while scoring one.
+    bf16x8 k0[KT], k1[KT];
+    load_group(first, k0);
+    int64_t e = first;
+    while (true) {
+        const bool more1 = e + 16 < last;
+        if (more1) load_group(e + 16, k1);
+        score_group(e, k0);
+        if (!more1) break;
+        const bool more2 = e + 32 < last;
+        if (more2) load_group(e + 32, k0);
+        score_group(e + 16, k1);
+        if (!more2) break;
+        e += 32;
+    }
+}
+
+// ------------------------------------------------------------------ burst
+// Workgroup = 4 waves x 64 entries of one sequence; it walks all T positions.
+// Keys of the wave's 64 entries stay in registers as B operands (32x32x16,
+// two entry tiles); the queries of position t (H <= 64 heads x D) are staged
+// in LDS once per workgroup, double-buffered, rows XOR-swizzled by 16-byte
+// chunk so the 32 heads read by one instruction hit distinct banks.
+template <int KS>
+__global__ __launch_bounds__(256) void k_score_burst(
+    const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
+    const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int T, int H,
+    int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
+    int reduce_max, float* __restrict__ z_out, float* __restrict__ prob_out) {
+    constexpr int D = 16 * KS;
+    constexpr int CH = D / 8;                 // 16-byte chunks per query row
+    constexpr int QCHUNKS = 64 * CH;          // per position (64 head slots)
+    __shared__ bf16x8 sq[2][QCHUNKS];
+    __shared__ float sw[2][64];
+
+    const int b = blockIdx.y;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t S = min((int64_t)seq_len[b], max_len);
+    const int64_t e_blk = (int64_t)blockIdx.x * 256;
+    if (e_blk >= S) return;
+    const int n32 = lane & 31;
+    const int g = lane >> 5;
+
+    // B operands: this wave's two tiles of 32 entries.
+    bf16x8 kb[2][KS];
+    int64_t ent[2];
+    const bf16* kbase = keys + key_row_start[b] * D + 8 * g;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+        ent[nt] = e_blk + wave * 64 + nt * 32 + n32;
+        const int64_t row = ent[nt] < S ? ent[nt] : e_blk;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kb[nt][ks] = load8(kbase + row * D + 16 * ks);
+    }
+
+    // Query staging: QCHUNKS 16-byte chunks per position, spread over 256 threads.
+    constexpr int PER = (QCHUNKS + 255) / 256;
+    bf16x8 qreg[PER];
+    float wreg = 0.0f;
+    auto fetch_q = [&](int t) {
+        const bf16* qt = q + ((int64_t)b * T + t) * H * D;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + 256 * i;
+            const int h = c / CH, ch = c % CH;
+            qreg[i] = (c < QCHUNKS && h < H) ? load8(qt + (int64_t)h * D + 8 * ch) : zero8();
+        }
+        if (tid < 64) wreg = tid < H ? w[((int64_t)b * T + t) * H + tid] : 0.0f;
+    };
+    auto stage_q = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int c = tid + 256 * i;
+            if (c < QCHUNKS) {
+                const int h = c / CH, ch = c % CH;
+                sq[buf][h * CH + (ch ^ (h & (CH - 1)))] = qreg[i];
+            }
+        }
+        if (tid < 64) sw[buf][tid] = wreg;
+    };
+
+    float mx[2] = {-INFINITY, -INFINITY};
+    const int64_t eo = entry_start[b];
+    fetch_q(0);
+    stage_q(0);
+    __syncthreads();
+    for (int t = 0; t < T; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < T) fetch_q(t + 1);
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const int h = 32 * mt + n32;
+                const int ch = 2 * ks + g;
+                const bf16x8 a = sq[buf][h * CH + (ch ^ (h & (CH - 1)))];
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(a, kb[nt][ks], acc[mt][nt]);
+            }
+        }
+        float s[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 wq = *reinterpret_cast<const f32x4*>(&sw[buf][32 * mt + 8 * j + 4 * g]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        s[nt] += wq[v] * fmaxf(acc[mt][nt][4 * j + v], 0.0f);
+            }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            s[nt] += __shfl_xor(s[nt], 32);
+            const float z = s[nt] + bias;
+            if (reduce_max) {
+                mx[nt] = fmaxf(mx[nt], z);
+            } else if (g == 0 && ent[nt] < S) {
+                const int64_t o = eo * T + (int64_t)t * S + ent[nt];
+                z_out[o] = z;
+                if (prob_out) prob_out[o] = sigmoidf(z);
+            }
+        }
+        if (t + 1 < T) stage_q(buf ^ 1);
+        __syncthreads();
+    }
+    if (reduce_max && g == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            if (ent[nt] < S) {
+                z_out[eo + ent[nt]] = mx[nt];
+                if (prob_out) prob_out[eo + ent[nt]] = sigmoidf(mx[nt]);
+            }
+    }
+}
+
+// ----------------------------------------------------------------- vector
+// One thread per entry; queries and weights of the sequence sit in LDS as fp32.
+template <typename E>
+__global__ __launch_bounds__(256) void k_score_vector(
+    const E* __restrict__ keys, const int64_t* __restrict__ key_row_start,
+    const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int T, int H,
+    int D, int64_t max_len, const E* __restrict__ q, const float* __restrict__ w, float bias,
+    int reduce_max, float* __restrict__ z_out, float* __restrict__ prob_out) {
+    extern __shared__ float smem[];
+    float* sq = smem;               // [T*H*D]
+    float* sw = smem + T * H * D;   // [T*H]
+    const int b = blockIdx.y;
+    const int nq = T * H * D;
+    for (int i = threadIdx.x; i < nq; i += blockDim.x) sq[i] = (float)q[(int64_t)b * nq + i];
+    for (int i = threadIdx.x; i < T * H; i += blockDim.x) sw[i] = w[(int64_t)b * T * H + i];
+    __syncthreads();
+    const int64_t S = min((int64_t)seq_len[b], max_len);
+    const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= S) return;
+    const E* row = keys + (key_row_start[b] + s) * D;
+    const int64_t eo = entry_start[b];
+    float m = -INFINITY;
+    for (int t = 0; t < T; ++t) {
+        float u = 0.0f;
+        for (int h = 0; h < H; ++h) {
+            const float* qh = sq + (t * H + h) * D;
+            float dot = 0.0f;
+            for (int d = 0; d < D; ++d) dot += qh[d] * (float)row[d];
+            u += sw[t * H + h] * fmaxf(dot, 0.0f);
+        }
+        const float z = u + bias;
+        if (reduce_max) {
+            m = fmaxf(m, z);
+        } else {
+            const int64_t o = eo * T + (int64_t)t * S + s;
+            z_out[o] = z;
+            if (prob_out) prob_out[o] = sigmoidf(z);
+        }
+    }
+    if (reduce_max) {
+        z_out[eo + s] = m;
+        if (prob_out) prob_out[eo + s] = sigmoidf(m);
+    }
+}
+
+template <int MT, int KT>
+static void launch_decode(dim3 grid, hipStream_t st, const void* keys, const int64_t* krs,
+                          const int32_t* lens, const int64_t* es, int H, int64_t max_len,
+                          const void* q, const float* w, float bias, float* z, float* p, int gpw) {
+    hipLaunchKernelGGL((k_score_decode<MT, KT>), grid, dim3(256), 0, st, (const bf16*)keys, krs,
+                       lens, es, H, max_len, (const bf16*)q, w, bias, z, p, gpw);
+}
+
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
+                               const int32_t* seq_len, const int64_t* entry_start, int B, int T,
+                               int H, int D, int64_t max_len, const void* q, const float* w,
+                               float bias, int reduce_max, float* z_out, float* prob_out,
+                               void* stream) {
+    clear_error();
+    if (!keys || !key_row_start || !seq_len || !entry_start || !q || !w || !z_out)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: a required pointer is NULL");
+    if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || max_len < 0)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: B=%d T=%d H=%d D=%d max_len=%lld", B, T,
+                    H, D, (long long)max_len);
+    if (dtype != LSA_DTYPE_F32 && dtype != LSA_DTYPE_BF16)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: unknown dtype %d", dtype);
+    if (!aligned16(keys) || !aligned16(q))
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: keys and q must be 16-byte aligned");
+    if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "lsa_index_score: B=%d > 65535", B);
+    if (max_len > (int64_t)1 << 31)
+        return fail(LSA_ERR_UNSUPPORTED, "lsa_index_score: max_len too large");
+    const bool mfma_shape = dtype == LSA_DTYPE_BF16 && H <= 64 && (D == 64 || D == 128);
+    if (!mfma_shape && (int64_t)T * H * (D + 1) > 16384)
+        return fail(LSA_ERR_UNSUPPORTED,
+                    "lsa_index_score: vector path needs T*H*(D+1) <= 16384 (T=%d H=%d D=%d)", T,
+                    H, D);
+    int cus = 0;
+    int rc = check_device(&cus);
+    if (rc != LSA_OK) return rc;
+    if (max_len == 0) return LSA_OK;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (mfma_shape && T == 1) {
+        const int64_t groups = ceil_div(max_len, 16);
+        // Aim for ~8 waves per CU across the batch; each wave takes >= 2 groups.
+        int64_t gpw = (groups * B) / ((int64_t)cus * 8);
+        gpw = gpw < 2 ? 2 : (gpw > 32 ? 32 : gpw);
+        gpw += gpw & 1;
+        dim3 grid((unsigned)ceil_div(groups, gpw * 4), (unsigned)B);
+        const int MT = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
+#define LSA_DEC(mt, kt)                                                                      \
+    launch_decode<mt, kt>(grid, st, keys, key_row_start, seq_len, entry_start, H, max_len, q, \
+                          w, bias, z_out, prob_out, (int)gpw)
+        // With one position the [T, S_b] layout and the reduced layout coincide.
+        if (D == 128) {
+            if (MT == 1) LSA_DEC(1, 4); else if (MT == 2) LSA_DEC(2, 4); else LSA_DEC(4, 4);
+        } else {
+            if (MT == 1) LSA_DEC(1, 2); else if (MT == 2) LSA_DEC(2, 2); else LSA_DEC(4, 2);
+        }
+#undef LSA_DEC
+        return launch_status("score_decode");
+    }
+    if (mfma_shape) {
+        dim3 grid((unsigned)ceil_div(max_len, 256), (unsigned)B);
+        if (D == 128)
+            hipLaunchKernelGGL(k_score_burst<8>, grid, dim3(256), 0, st, (const bf16*)keys,
+                               key_row_start, seq_len, entry_start, T, H, max_len, (const bf16*)q,
+                               w, bias, reduce_max, z_out, prob_out);
+        else
+            hipLaunchKernelGGL(k_score_burst<4>, grid, dim3(256), 0, st, (const bf16*)keys,
+                               key_row_start, seq_len, entry_start, T, H, max_len, (const bf16*)q,
+                               w, bias, reduce_max, z_out, prob_out);
+        return launch_status("score_burst");
+    }
+    dim3 grid((unsigned)ceil_div(max_len, 256), (unsigned)B);
+    const size_t shm = sizeof(float) * ((size_t)T * H * D + (size_t)T * H);
+    if (dtype == LSA_DTYPE_F32)
+        hipLaunchKernelGGL(k_score_vector<float>, grid, dim3(256), shm, st, (const float*)keys,
+                           key_row_start, seq_len, entry_start, T, H, D, max_len, (const float*)q,
+                           w, bias, reduce_max, z_out, prob_out);
+    else
+        hipLaunchKernelGGL(k_score_vector<bf16>, grid, dim3(256), shm, st, (const bf16*)keys,
+                           key_row_start, seq_len, entry_start, T, H, D, max_len, (const bf16*)q,
+                           w, bias, reduce_max, z_out, prob_out);
+    return launch_status("score_vector");
+}

@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports what include/lsa.h declares, and rejects bad arguments on
+the host before touching a GPU (no compute call is made here)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from lookahead_sparse_kv_amd import binding
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(REPO, "include", "lsa.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("liblsa.so is not built; run python -m lookahead_sparse_kv_amd.build")
+    return binding.load_library()
+
+
+def test_header_declares_the_four_calls():
+    syms = declared_symbols()
+    for s in ("lsa_index_score", "lsa_select_compact", "lsa_topk", "lsa_sparse_attend",
+              "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"):
+        assert s in syms
+    assert sorted(binding.EXPORTED) == syms
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (lsa_[a-z_]+)\b", out))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert hasattr(lib, s)
+
+
+def test_library_is_built_for_gfx950_only():
+    """The embedded device code objects name the gfx950 target and no other."""
+    data = open(binding.LIB_PATH, "rb").read()
+    targets = set(re.findall(rb"amdgcn-amd-amdhsa-+(gfx[0-9a-f]+)", data))
+    assert targets == {b"gfx950"}, targets
+
+
+def test_status_strings_and_version(lib):
+    assert lib.lsa_version() >= 100
+    for code in (0, -1, -2, -3, -4):
+        assert lib.lsa_status_string(code)
+    assert lib.lsa_status_string(-99) == b"unknown status"
+
+
+def test_index_score_validation(lib):
+    P = FAKE
+    f = lib.lsa_index_score
+    assert f(None, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1
+    assert b"NULL" in lib.lsa_last_error()
+    assert f(P, 1, P, P, P, 0, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1   # B = 0
+    assert f(P, 1, P, P, P, 1, 1, 64, -5, 10, P, P, 0.0, 0, P, None, None) == -1   # D < 0
+    assert f(P, 7, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1  # dtype
+    assert f(MISALIGNED, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1
+    assert b"aligned" in lib.lsa_last_error()
+    # vector path envelope
+    assert f(P, 0, P, P, P, 1, 64, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -2
+    assert f(P, 1, P, P, P, 70000, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -2
+
+
+def test_select_validation(lib):
+    P = FAKE
+    f = lib.lsa_select_compact
+    assert f(None, P, P, 1, 10, 0.0, P, P, P, 1 << 20, None) == -1
+    assert f(P, P, P, 0, 10, 0.0, P, P, P, 1 << 20, None) == -1
+    need = lib.lsa_workspace_bytes(1, 4, 0, 0, 0, 100000, 0, 0)
+    assert need >= 4 * 4
+    assert f(P, P, P, 4, 100000, 0.0, P, P, P, need - 1, None) == -3
+    assert f(P, P, P, 4, 100000, 0.0, P, P, None, need, None) == -3
+
+
+def test_topk_validation(lib):
+    P = FAKE
+    f = lib.lsa_topk
+    assert f(P, P, P, 1, 10, P, P, 0, P, P, None, 0, None) == -1        # k = 0
+    assert f(P, P, P, 1, 10, P, P, -3, P, P, None, 0, None) == -1
+    assert f(P, P, P, 1, 10, P, P, 70000, P, P, None, 0, None) == -2    # k too large
+    assert f(None, P, P, 1, 10, P, P, 4, P, P, None, 0, None) == -1
+    need = lib.lsa_workspace_bytes(2, 2, 0, 0, 0, 200000, 2048, 0)
+    assert need > 0
+    assert f(P, P, P, 2, 200000, P, P, 2048, P, P, P, need - 4, None) == -3
+
+
+def test_attend_validation(lib):
+    P = FAKE
+    f = lib.lsa_sparse_attend
+    args = [P, 1, 8, 1, 64, 512, P, P, P, P, 2048, P, P, P, 3907, 0.04, P, None, P, 1 << 30, None]
+    a = list(args); a[0] = None
+    assert f(*a) == -1
+    a = list(args); a[12] = None                 # hca without row starts
+    assert f(*a) == -1
+    a = list(args); a[10] = 0                    # k = 0
+    assert f(*a) == -1
+    a = list(args); a[0] = MISALIGNED
+    assert f(*a) == -1
+    a = list(args); a[5] = 2048                  # Dl too large
+    assert f(*a) == -2
+    a = list(args); a[15] = float("nan")
+    assert f(*a) == -1
+    need = lib.lsa_workspace_bytes(3, 8, 1, 64, 512, 0, 2048, 3907)
+    assert need > 0
+    a = list(args); a[19] = need - 1
+    assert f(*a) == -3
+
+
+def test_workspace_sizes(lib):
+    assert lib.lsa_workspace_bytes(9, 1, 1, 1, 1, 1, 1, 1) == 0
+    assert lib.lsa_workspace_bytes(1, 0, 0, 0, 0, 10, 0, 0) == 0
+    # top-k needs a global area only when a candidate list can exceed the LDS capacity
+    assert lib.lsa_workspace_bytes(2, 8, 0, 0, 0, 32768, 2048, 0) == 0
+    assert lib.lsa_workspace_bytes(2, 8, 0, 0, 0, 32769, 2048, 0) == 8 * 32769 * 4
+    # one (b, t) pair per CU-sized split plan: B*T large -> no split, no workspace
+    assert lib.lsa_workspace_bytes(3, 16, 64, 64, 512, 0, 2048, 0) == 0
