@@ -24,6 +24,8 @@ COMMON = [
     "-std=c++17", "-O3", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions stay off: plain fp32 arithmetic only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in architectural VGPRs (no AGPR round trips in loops)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

@@ -22,6 +22,9 @@
 
 namespace lsa {
 
+constexpr int kScoreDepth = 3;         // key groups in flight per wave (decode kernel)
+constexpr int kScoreGroupsPerWave = 32;
+
 // ----------------------------------------------------------------- decode
 // One wave scores groups of 16 consecutive entries of one sequence.
 //   lane l: n = l%16 selects the entry, g = l/16 selects 8 of each 32 dims.
@@ -36,6 +39,7 @@ __global__ __launch_bounds__(256) void k_score_decode(
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
     float* __restrict__ z_out, float* __restrict__ prob_out, int groups_per_wave) {
     constexpr int D = 32 * KT;
+    constexpr int DEPTH = kScoreDepth;      // groups of 16 entries in flight per wave
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -46,69 +50,66 @@ __global__ __launch_bounds__(256) void k_score_decode(
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
+    const bf16* kbase = keys + key_row_start[b] * D + 8 * g;
+    auto load_group = [&](int64_t e0, bf16x8 (&kb)[KT]) {
+        const int64_t n = e0 + n16;
+        const int64_t row = n < last ? n : e0;  // e0 < last: tail lanes re-read a valid row
+        const bf16* p = kbase + row * D;
+#pragma unroll
+        for (int kk = 0; kk < KT; ++kk) kb[kk] = load8(p + 32 * kk);
+    };
+    // key loads go out first; the query operands follow while they are in flight
+    bf16x8 kb[DEPTH][KT];
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+        if (first + 16 * i < last) load_group(first + 16 * i, kb[i]);
+
     bf16x8 qa[MT][KT];
     float wv[MT][4];
     const bf16* qb = q + (int64_t)b * H * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int head = 16 * mt + n16;
+        const int head = min(16 * mt + n16, H - 1);
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk)
-            qa[mt][kk] = head < H ? load8(qb + (int64_t)head * D + 32 * kk + 8 * g) : zero8();
+        for (int kk = 0; kk < KT; ++kk) qa[mt][kk] = load8(qb + (int64_t)head * D + 32 * kk + 8 * g);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int hv = 16 * mt + 4 * g + v;
+            // padded heads carry zero weight, so their (duplicated) products drop out
             wv[mt][v] = hv < H ? w[(int64_t)b * H + hv] : 0.0f;
         }
     }
-
-    const bf16* kbase = keys + key_row_start[b] * D + 8 * g;
     const int64_t eo = entry_start[b];
 
-    auto load_group = [&](int64_t e0, bf16x8 (&kb)[KT]) {
-        const int64_t n = e0 + n16;
-        const int64_t row = n < last ? n : e0;  // e0 < last always
-        const bf16* p = kbase + row * D;
+    for (int64_t e = first; e < last; e += 16 * DEPTH) {
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) kb[kk] = load8(p + 32 * kk);
-    };
-    auto score_group = [&](int64_t e0, const bf16x8 (&kb)[KT]) {
-        f32x4 acc[MT];
+        for (int i = 0; i < DEPTH; ++i) {
+            const int64_t e0 = e + 16 * i;
+            if (e0 >= last) break;
+            f32x4 acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk)
+            for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(qa[mt][kk], kb[kk], acc[mt]);
-        float s = 0.0f;
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(qa[mt][kk], kb[i][kk], acc[mt]);
+            // refill this ring slot with the group DEPTH steps ahead
+            const int64_t en = e0 + 16 * DEPTH;
+            if (en < last) load_group(en, kb[i]);
+            float sacc = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) s += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
-        s += __shfl_xor(s, 16);
-        s += __shfl_xor(s, 32);
-        const int64_t n = e0 + n16;
-        if (g == 0 && n < last) {
-            const float z = s + bias;
-            z_out[eo + n] = z;
-            if (prob_out) prob_out[eo + n] = sigmoidf(z);
+                for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
+            sacc += __shfl_xor(sacc, 16);
+            sacc += __shfl_xor(sacc, 32);
+            const int64_t n = e0 + n16;
+            if (g == 0 && n < last) {
+                const float z = sacc + bias;
+                z_out[eo + n] = z;
+                if (prob_out) prob_out[eo + n] = sigmoidf(z);
+            }
         }
-    };
-
-    // Two groups in flight per wave: prefetch the next group while scoring one.
-    bf16x8 k0[KT], k1[KT];
-    load_group(first, k0);
-    int64_t e = first;
-    while (true) {
-        const bool more1 = e + 16 < last;
-        if (more1) load_group(e + 16, k1);
-        score_group(e, k0);
-        if (!more1) break;
-        const bool more2 = e + 32 < last;
-        if (more2) load_group(e + 32, k0);
-        score_group(e + 16, k1);
-        if (!more2) break;
-        e += 32;
     }
 }
 
@@ -329,10 +330,10 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
 
     if (mfma_shape && T == 1) {
         const int64_t groups = ceil_div(max_len, 16);
-        // Aim for ~8 waves per CU across the batch; each wave takes >= 2 groups.
-        int64_t gpw = (groups * B) / ((int64_t)cus * 8);
-        gpw = gpw < 2 ? 2 : (gpw > 32 ? 32 : gpw);
-        gpw += gpw & 1;
+        // Long-lived waves (each loads its query operands once): up to 32 groups of 16
+        // entries per wave, fewer when the batch is too small to give every CU ~4 waves.
+        int64_t gpw = (groups * B) / ((int64_t)cus * 4);
+        gpw = gpw < 1 ? 1 : (gpw > kScoreGroupsPerWave ? kScoreGroupsPerWave : gpw);
         dim3 grid((unsigned)ceil_div(groups, gpw * 4), (unsigned)B);
         const int MT = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
 #define LSA_DEC(mt, kt)                                                                      \

@@ -57,7 +57,21 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
                           int* scratch, int* sh) {
     auto P = [](int j) { return IN_LDS ? j + (j >> 5) : j; };
     const int tid = threadIdx.x;
-    for (int j = tid; j < n; j += kTkThreads) keys[P(j)] = order_key(rb[cand[j]]);
+    // Gather the keys, 8 independent loads in flight per thread (indices are
+    // clamped instead of branched on, so no load waits for the previous one).
+    for (int j0 = tid; j0 < n; j0 += 8 * kTkThreads) {
+        int c[8];
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cand[min(j0 + u * kTkThreads, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = rb[c[u]];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u * kTkThreads;
+            if (j < n) keys[P(j)] = order_key(v[u]);
+        }
+    }
     __syncthreads();
 
     uint32_t prefix = 0, pmask = 0;
@@ -119,13 +133,21 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
     const int take_eq = max(0, min(need - eq_base, eq));
     int pos = block_excl_scan(gt + take_eq, scratch, &tot);
     int eq_seen = eq_base;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t u = keys[P(j)];
-        if (u > U) {
-            out[pos++] = cand[j];
-        } else if (u == U) {
-            if (eq_seen < need) out[pos++] = cand[j];
-            ++eq_seen;
+    for (int jb = j0; jb < j1; jb += 8) {
+        int c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = cand[min(jb + u, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + u;
+            if (j >= j1) break;
+            const uint32_t key = keys[P(j)];
+            if (key > U) {
+                out[pos++] = c[u];
+            } else if (key == U) {
+                if (eq_seen < need) out[pos++] = c[u];
+                ++eq_seen;
+            }
         }
     }
 }
