@@ -10,7 +10,7 @@ Prints one JSON line.  `value` = indexer scores per second of whole steps
 kernel, the dominant one by bytes; the attention kernel gets a second one.
 Inputs are resident in HBM before timing; key and latent pools are replicated
 and rotated so each timed launch reads memory the 256 MB on-die cache does
-not hold.
+not hold.  Timed work is replayed from HIP graphs captured on one stream.
 """
 from __future__ import annotations
 
@@ -74,22 +74,28 @@ def read_traffic(kernel: str, workload: str, src: str):
         return None
 
 
-def timed(torch, stream, fn, reps, intervals=7, warm=2):
-    """Median per-launch time (s) of `fn(i)` over `intervals` runs of `reps` launches,
-    measured with HIP events recorded on `stream` (the stream the kernels run on)."""
+def capture(torch, stream, fns):
+    """One HIP graph holding the launches of `fns` in order (on `stream`)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for f in fns:
+            f()
+    return g
+
+
+def timed_graph(torch, stream, g, launches, intervals=7, warm=2):
+    """Median seconds per launch over `intervals` replays of graph `g`, which holds
+    `launches` launches; HIP events recorded on `stream`, where the graph runs."""
     res = []
-    i = 0
     for it in range(warm + intervals):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(reps):
-            fn(i)
-            i += 1
+        g.replay()
         e1.record(stream)
         e1.synchronize()
         if it >= warm:
-            res.append(e0.elapsed_time(e1) * 1e-3 / reps)
+            res.append(e0.elapsed_time(e1) * 1e-3 / launches)
     return statistics.median(res)
 
 
@@ -163,26 +169,38 @@ def main():
                               "copy_bytes": args.copy_bytes}))
             return
 
-        for i in range(args.warmup):
+        # Steps and per-kernel runs are replayed from HIP graphs (no host work in
+        # the timed region); replicas rotate so reads come from HBM, not the cache.
+        nrot = max(rk, rl)
+        for i in range(max(args.warmup, 1)):
             p.step(i)
+        torch.cuda.synchronize()
+        step_graphs = [capture(torch, stream, [lambda i=i: p.step(i)]) for i in range(nrot)]
+        for i in range(args.warmup):
+            step_graphs[i % nrot].replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         e0.record(stream)
         for i in range(args.steps):
-            p.step(i)
+            step_graphs[i % nrot].replay()
         e1.record(stream)
         torch.cuda.synchronize()
         step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
 
-        # per-kernel launch durations (same stream, HIP events), rotating replicas
+        # per-kernel launch durations: graphs of R back-to-back launches of one call
         def reps_for(est_s):
-            return args.kernel_reps or max(5, int(1e-3 / max(est_s, 1e-7)) + 1)
-        t_score = timed(torch, stream, lambda i: p.score(i), reps_for(step_s / 2))
-        t_select = timed(torch, stream, lambda i: p.select(), reps_for(1e-5))
-        t_topk = timed(torch, stream, lambda i: p.topk(), reps_for(2e-5))
-        t_attend = timed(torch, stream, lambda i: p.attend(i), reps_for(step_s / 4))
+            return args.kernel_reps or max(8, min(200, int(2e-3 / max(est_s, 1e-6)) + 1))
+        r = reps_for(step_s / 2)
+        t_score = timed_graph(torch, stream, capture(
+            torch, stream, [lambda i=i: p.score(i) for i in range(r)]), r)
+        r = reps_for(1e-5)
+        t_select = timed_graph(torch, stream, capture(torch, stream, [p.select] * r), r)
+        t_topk = timed_graph(torch, stream, capture(torch, stream, [p.topk] * r), r)
+        r = reps_for(step_s / 4)
+        t_attend = timed_graph(torch, stream, capture(
+            torch, stream, [lambda i=i: p.attend(i) for i in range(r)]), r)
+        del step_graphs
 
     torch.cuda.synchronize()
     counts = p.cand_count.cpu().numpy()

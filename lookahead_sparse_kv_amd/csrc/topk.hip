@@ -8,8 +8,9 @@
 //
 // One workgroup (1024 threads) per sequence.  Keys are mapped to
 // order-preserving uint32, staged in LDS (up to kCap candidates; larger sets
-// use a global scratch area), and a radix select over four 8-bit digits finds
-// the k-th key U and how many keys equal to U to take.  A last ordered pass
+// use a global scratch area), and a radix select over 8-bit digits -- starting
+// below the bits every candidate shares -- finds the k-th key U and how many
+// keys equal to U to take.  A last ordered pass
 // keeps every key > U and the first `need` keys == U (the smallest indices,
 // since candidates are in ascending order), compacted with workgroup scans.
 #include "common.hpp"
@@ -20,6 +21,7 @@ constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
 constexpr int kCap = 32768;                      // candidates held in LDS
 constexpr int kCapPadded = kCap + kCap / 32;     // one pad word per 32 (bank spread)
+constexpr int kHistCopies = 16;                  // lane-spread copies of each radix bin
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -59,6 +61,8 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
     const int tid = threadIdx.x;
     // Gather the keys, 8 independent loads in flight per thread (indices are
     // clamped instead of branched on, so no load waits for the previous one).
+    // The AND and OR of all keys give the bits every candidate shares.
+    uint32_t kand = ~0u, kor = 0u;
     for (int j0 = tid; j0 < n; j0 += 8 * kTkThreads) {
         int c[8];
         float v[8];
@@ -69,26 +73,67 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = j0 + u * kTkThreads;
-            if (j < n) keys[P(j)] = order_key(v[u]);
+            const uint32_t key = order_key(v[u]);
+            kand &= key;
+            kor |= key;
+            if (j < n) keys[P(j)] = key;
         }
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        kand &= (uint32_t)__shfl_xor((int)kand, off);
+        kor |= (uint32_t)__shfl_xor((int)kor, off);
+    }
+    if ((tid & 63) == 0) {
+        scratch[tid >> 6] = (int)kand;
+        scratch[kTkWaves + (tid >> 6)] = (int)kor;
+    }
     __syncthreads();
+    kand = ~0u;
+    kor = 0u;
+    for (int i = 0; i < kTkWaves; ++i) {
+        kand &= (uint32_t)scratch[i];
+        kor |= (uint32_t)scratch[kTkWaves + i];
+    }
 
-    uint32_t prefix = 0, pmask = 0;
+    // Radix select over the bits where candidates differ, most significant
+    // first, 8 bits per pass: histogram the digit among keys that match the
+    // prefix fixed so far, then keep the digit holding the need-th largest key.
+    const uint32_t diff = kand ^ kor;
+    const int top = diff ? 31 - __clz(diff) : -1;          // highest differing bit
+    uint32_t pmask = top >= 31 ? 0u : (~0u << (top + 1));
+    uint32_t prefix = kand & pmask;
     int need = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
+    for (int hi = top + 1; hi > 0;) {
+        const int lo = max(hi - 8, 0);
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        __syncthreads();                                   // previous pass done with hist/sh
+        for (int i = tid; i < 256 * kHistCopies; i += kTkThreads) hist[i] = 0;
         __syncthreads();
+        // kHistCopies copies of every bin, picked by lane, so lanes counting the
+        // same digit hit different banks instead of serialising on one word
+        const int copy = tid & (kHistCopies - 1);
         for (int j = tid; j < n; j += kTkThreads) {
             const uint32_t u = keys[P(j)];
-            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+            if ((u & pmask) == prefix) atomicAdd(&hist[((u >> lo) & dmask) * kHistCopies + copy], 1u);
         }
         __syncthreads();
         if (tid < 64) {
             // lane l owns digits 4l..4l+3; find the digit d with
             // (#keys with digit > d) < need <= (#keys with digit >= d).
-            const int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2],
-                      c3 = hist[4 * tid + 3];
+            int cnt[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4* hq = reinterpret_cast<const u32x4*>(&hist[(4 * tid + q) * kHistCopies]);
+                int t = 0;
+#pragma unroll
+                for (int i = 0; i < kHistCopies / 4; ++i) {
+                    const u32x4 v = hq[i];
+                    t += (int)(v[0] + v[1] + v[2] + v[3]);
+                }
+                cnt[q] = t;
+            }
+            const int c0 = cnt[0], c1 = cnt[1], c2 = cnt[2], c3 = cnt[3];
             const int tot = c0 + c1 + c2 + c3;
             int suf = tot;  // inclusive suffix sum over lanes >= tid
 #pragma unroll
@@ -112,16 +157,21 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
             }
         }
         __syncthreads();
-        prefix |= (uint32_t)sh[0] << shift;
-        pmask |= 0xFFu << shift;
+        prefix |= (uint32_t)sh[0] << lo;
+        pmask |= dmask << lo;
         need = sh[1];
-        __syncthreads();
+        hi = lo;
     }
     const uint32_t U = prefix;
 
-    // Ordered compaction: thread t walks candidates [t*per, (t+1)*per).
+    // Ordered compaction: thread t walks candidates [t*per, (t+1)*per).  The
+    // first 16 candidate indices of the run are fetched now, so their latency
+    // hides behind the counting and the two workgroup scans.
     const int per = (n + kTkThreads - 1) / kTkThreads;
     const int j0 = min(tid * per, n), j1 = min(j0 + per, n);
+    int cpre[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) cpre[u] = cand[min(j0 + u, n - 1)];
     int gt = 0, eq = 0;
     for (int j = j0; j < j1; ++j) {
         const uint32_t u = keys[P(j)];
@@ -133,22 +183,25 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
     const int take_eq = max(0, min(need - eq_base, eq));
     int pos = block_excl_scan(gt + take_eq, scratch, &tot);
     int eq_seen = eq_base;
-    for (int jb = j0; jb < j1; jb += 8) {
+    auto emit = [&](int j, int cj) {
+        const uint32_t key = keys[P(j)];
+        if (key > U) {
+            out[pos++] = cj;
+        } else if (key == U) {
+            if (eq_seen < need) out[pos++] = cj;
+            ++eq_seen;
+        }
+    };
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+        if (j0 + u < j1) emit(j0 + u, cpre[u]);
+    for (int jb = j0 + 16; jb < j1; jb += 8) {
         int c[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) c[u] = cand[min(jb + u, n - 1)];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = jb + u;
-            if (j >= j1) break;
-            const uint32_t key = keys[P(j)];
-            if (key > U) {
-                out[pos++] = c[u];
-            } else if (key == U) {
-                if (eq_seen < need) out[pos++] = c[u];
-                ++eq_seen;
-            }
-        }
+        for (int u = 0; u < 8; ++u)
+            if (jb + u < j1) emit(jb + u, c[u]);
     }
 }
 
@@ -158,8 +211,8 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
     const int32_t* __restrict__ cand_count, int k, int32_t* __restrict__ topk_idx,
     int32_t* __restrict__ topk_count, uint32_t* __restrict__ gkeys) {
     __shared__ uint32_t skeys[kCapPadded];
-    __shared__ unsigned hist[256];
-    __shared__ int scratch[kTkWaves];
+    __shared__ __attribute__((aligned(16))) unsigned hist[256 * kHistCopies];
+    __shared__ int scratch[2 * kTkWaves];
     __shared__ int sh[2];
     const int b = blockIdx.x;
     const int64_t S = min((int64_t)seq_len[b], max_len);
