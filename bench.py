@@ -225,8 +225,10 @@ def main():
                         read_traffic("score_decode", args.workload, "score.hip"))
     else:
         roofline = roof("mfma", score_flops, t_score, BF16_PEAK_TFLOPS, "TFLOP/s", None)
+    ta, tc = (read_traffic("attend", args.workload, "attend.hip"),
+              read_traffic("attend_combine", args.workload, "attend.hip"))
     roof_att = roof("hbm", att_alg_bytes, t_attend, HBM_PEAK_GBS, "GB/s",
-                    read_traffic("attend", args.workload, "attend.hip"))
+                    None if ta is None else ta + (tc or 0.0))
     roof_att["mfma_frac"] = round(att_flops / t_attend / 1e12 / BF16_PEAK_TFLOPS, 4)
 
     line = {
