@@ -22,47 +22,81 @@
 
 namespace lsa {
 
-constexpr int kScoreDepth = 3;         // key groups in flight per wave (decode kernel)
+constexpr int kScoreRing = 4;          // LDS ring slots per wave (decode kernel)
+// cache-policy operand of the direct-to-LDS loads: keys are read once, so they are
+// fetched as streaming (nontemporal) data
+constexpr int kNonTemporal = 2;
 constexpr int kScoreGroupsPerWave = 32;
+
+// vmcnt(n) with the other counters left alone (n <= 63).  Stores count too, so
+// waiting on loads by this bound is conservative.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_score() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 // ----------------------------------------------------------------- decode
 // One wave scores groups of 16 consecutive entries of one sequence.
-//   lane l: n = l%16 selects the entry, g = l/16 selects 8 of each 32 dims.
-//   A (queries) stays in registers for the whole wave: MT x KT operands.
-//   B (keys): for k-step kk the lane loads dims 32kk + 8g .. +7 of its entry,
-//   so one load instruction reads 64 contiguous bytes of 16 key rows.
+//   Keys stream HBM -> a wave-private LDS ring with direct-to-LDS loads, each
+//   instruction moving 1 KiB of consecutive rows (4 rows of 256 B), up to
+//   NB groups ahead of use.  Inside a staged row, 16-byte slot p holds logical
+//   slot p ^ (row & 15), so the operand reads below are bank-conflict-free.
+//   MFMA operands: lane l, n = l%16 selects the entry, g = l/16 selects 8 of
+//   each 32 dims; A (queries) stays in registers for the whole wave; B (keys)
+//   for k-step kk is dims 32kk + 8g .. +7 of entry n.
 //   D[4g+v][n] of head tile mt is head 16mt + 4g + v of entry n.
 template <int MT, int KT>
 __global__ __launch_bounds__(256) void k_score_decode(
     const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int H,
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
-    float* __restrict__ z_out, float* __restrict__ prob_out, int groups_per_wave) {
+    float* __restrict__ z_out, float* __restrict__ prob_out) {
     constexpr int D = 32 * KT;
-    constexpr int DEPTH = kScoreDepth;      // groups of 16 entries in flight per wave
+    constexpr int SLOTS = D / 8;                 // 16-byte slots per key row
+    constexpr int RPI = 64 / SLOTS;              // rows per direct-to-LDS instruction
+    constexpr int DMAG = 16 / RPI;               // instructions per group of 16 rows
+    constexpr int NB = kScoreRing;               // ring slots per wave
+    static_assert(SLOTS >= 16 || SLOTS == 8, "row layout");
+    __shared__ __attribute__((aligned(16))) bf16 ring[4][NB][16 * D];
+
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t S = min((int64_t)seq_len[b], max_len);
-    const int64_t first = ((int64_t)blockIdx.x * 4 + wave) * (int64_t)groups_per_wave * 16;
-    if (first >= S) return;
-    const int64_t last = min(first + (int64_t)groups_per_wave * 16, S);
+    // The waves of one sequence deal its groups round robin, so at any moment the
+    // chip reads a compact window of the sequence rather than thousands of
+    // separate streams.
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    const int64_t G = (S + 15) / 16;
+    if (gw >= G) return;
+    const int ngroups = (int)((G - gw + nw - 1) / nw);
+    const int64_t last = S;
     const int n16 = lane & 15;
     const int g = lane >> 4;
 
-    const bf16* kbase = keys + key_row_start[b] * D + 8 * g;
-    auto load_group = [&](int64_t e0, bf16x8 (&kb)[KT]) {
-        const int64_t n = e0 + n16;
-        const int64_t row = n < last ? n : e0;  // e0 < last: tail lanes re-read a valid row
-        const bf16* p = kbase + row * D;
+    const bf16* kbase = keys + key_row_start[b] * D;
+    bf16* myring = &ring[wave][0][0];
+    // Group i of this wave is group gw + nw*i of the sequence and goes to ring slot
+    // i % NB; rows past the sequence re-read its last row.
+    auto issue = [&](int i) {
+        const int64_t e0 = 16 * (gw + nw * (int64_t)i);
+        bf16* slot = myring + (i % NB) * 16 * D;
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) kb[kk] = load8(p + 32 * kk);
+        for (int j = 0; j < DMAG; ++j) {
+            const int r = RPI * j + lane / SLOTS;             // row inside the group
+            const int64_t e = min(e0 + r, last - 1);
+            const int ps = lane % SLOTS;
+            const bf16* src = kbase + e * D + 8 * (ps ^ (r & (SLOTS - 1) & 15));
+            __builtin_amdgcn_global_load_lds(
+                (const void*)src, (__attribute__((address_space(3))) void*)(slot + RPI * j * D),
+                16, 0, kNonTemporal);
+        }
     };
-    // key loads go out first; the query operands follow while they are in flight
-    bf16x8 kb[DEPTH][KT];
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i)
-        if (first + 16 * i < last) load_group(first + 16 * i, kb[i]);
+    for (int i = 0; i < NB; ++i)
+        if (i < ngroups) issue(i);
 
     bf16x8 qa[MT][KT];
     float wv[MT][4];
@@ -80,35 +114,43 @@ __global__ __launch_bounds__(256) void k_score_decode(
         }
     }
     const int64_t eo = entry_start[b];
+    const int rsw = n16 & (SLOTS - 1) & 15;
 
-    for (int64_t e = first; e < last; e += 16 * DEPTH) {
+    for (int i = 0; i < ngroups; ++i) {
+        // wait until group i's copies landed: later groups' copies may stay in flight
+        // (vector memory operations complete in issue order)
+        const int after = min(ngroups - 1, i + NB - 1) - i;
+        static_assert(NB <= 4, "waits below cover up to three later groups");
+        if (after >= 3) wait_vmcnt_score<3 * DMAG>();
+        else if (after == 2) wait_vmcnt_score<2 * DMAG>();
+        else if (after == 1) wait_vmcnt_score<DMAG>();
+        else wait_vmcnt_score<0>();
+        const bf16* slot = myring + (i % NB) * 16 * D + n16 * D;
+        bf16x8 kb[KT];
 #pragma unroll
-        for (int i = 0; i < DEPTH; ++i) {
-            const int64_t e0 = e + 16 * i;
-            if (e0 >= last) break;
-            f32x4 acc[MT];
+        for (int kk = 0; kk < KT; ++kk)
+            kb[kk] = *reinterpret_cast<const bf16x8*>(slot + 8 * ((4 * kk + g) ^ rsw));
+        f32x4 acc[MT];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KT; ++kk)
+        for (int kk = 0; kk < KT; ++kk)
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(qa[mt][kk], kb[i][kk], acc[mt]);
-            // refill this ring slot with the group DEPTH steps ahead
-            const int64_t en = e0 + 16 * DEPTH;
-            if (en < last) load_group(en, kb[i]);
-            float sacc = 0.0f;
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(qa[mt][kk], kb[kk], acc[mt]);
+        // the operands are in registers: refill slot i % NB with group i + NB
+        if (i + NB < ngroups) issue(i + NB);
+        float sacc = 0.0f;
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
-            sacc += __shfl_xor(sacc, 16);
-            sacc += __shfl_xor(sacc, 32);
-            const int64_t n = e0 + n16;
-            if (g == 0 && n < last) {
-                const float z = sacc + bias;
-                z_out[eo + n] = z;
-                if (prob_out) prob_out[eo + n] = sigmoidf(z);
-            }
+            for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
+        sacc += __shfl_xor(sacc, 16);
+        sacc += __shfl_xor(sacc, 32);
+        const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
+        if (g == 0 && n < last) {
+            const float z = sacc + bias;
+            z_out[eo + n] = z;
+            if (prob_out) prob_out[eo + n] = sigmoidf(z);
         }
     }
 }
@@ -290,9 +332,9 @@ __global__ __launch_bounds__(256) void k_score_vector(
 template <int MT, int KT>
 static void launch_decode(dim3 grid, hipStream_t st, const void* keys, const int64_t* krs,
                           const int32_t* lens, const int64_t* es, int H, int64_t max_len,
-                          const void* q, const float* w, float bias, float* z, float* p, int gpw) {
+                          const void* q, const float* w, float bias, float* z, float* p) {
     hipLaunchKernelGGL((k_score_decode<MT, KT>), grid, dim3(256), 0, st, (const bf16*)keys, krs,
-                       lens, es, H, max_len, (const bf16*)q, w, bias, z, p, gpw);
+                       lens, es, H, max_len, (const bf16*)q, w, bias, z, p);
 }
 
 }  // namespace lsa
@@ -338,7 +380,7 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
         const int MT = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
 #define LSA_DEC(mt, kt)                                                                      \
     launch_decode<mt, kt>(grid, st, keys, key_row_start, seq_len, entry_start, H, max_len, q, \
-                          w, bias, z_out, prob_out, (int)gpw)
+                          w, bias, z_out, prob_out)
         // With one position the [T, S_b] layout and the reduced layout coincide.
         if (D == 128) {
             if (MT == 1) LSA_DEC(1, 4); else if (MT == 2) LSA_DEC(2, 4); else LSA_DEC(4, 4);
