@@ -7,30 +7,31 @@
 // entry carries one latent row that serves as key and value for all query
 // heads (multi-query form over a shared latent).
 //
-// Matrix-core kernel (bf16, Hq <= 64, Dl = NW * DPW):
-//   workgroup = one (b, t, group of 32 query heads, row split); its NW waves
-//   split the latent dimension, wave w owning dims [w*DPW, (w+1)*DPW)
-//   (8 waves x 64 dims for Dl = 512: two waves per SIMD hide each other's
-//   latencies).  Per chunk of 32 attended rows:
-//     1. each wave copies its DPW-wide slice of the 32 rows from HBM straight
-//        into an LDS ring slot (direct-to-LDS loads, 2-3 chunks in flight);
-//     2. partial logits S_w = Q[:, dims_w] . C[:, dims_w]^T (64 heads x 32);
-//     3. the partial logits of the NW waves meet in LDS; each wave finishes
-//        the softmax of 32/NW heads (online, base-2, lazily rescaled) and
-//        publishes P (bf16) and the rescale factors;
-//     4. O[:, dims_w] += P . C[:, dims_w] with C read transposed from the same
-//        slot (transposing LDS reads).
-//   The row slice each wave needs for P.V is exactly the slice it loaded, so
-//   only the small logit tiles cross waves.  Rows are split across
-//   workgroups when B*T is small; a combine kernel merges the splits by their
-//   log-sum-exp.
+// Matrix-core kernel (bf16, Dl in {128, 256, 512}).  Every query head of every
+// position of sequence b attends to the same rows, so the (position, head)
+// pairs of b are flattened into M = T * Hq query rows.  A workgroup of four
+// waves takes one (b, group of 32 query rows, row split) and walks its rows in
+// chunks of 32:
+//   1. the chunk's rows are copied from HBM straight into an LDS ring slot
+//      (direct-to-LDS loads, each wave copying a quarter; NB-1 chunks ahead);
+//   2. S = Q K^T: wave w owns the 16 x 16 tile (query rows 16(w&1).., chunk
+//      rows 16(w>>1)..) over the full latent depth, Q held in registers, so
+//      no partial logits cross waves;
+//   3. online softmax in base 2: per-query-row maxima and sums of the two row
+//      tiles meet in LDS, P (bf16) is published there;
+//   4. O[:, dims_w] += P C[:, dims_w]: wave w owns Dl/4 latent dims of all 32
+//      query rows; C^T operands come from transposing LDS reads of the slot.
+// Rows are split across workgroups when B * T * Hq is small; a combine kernel
+// merges the splits by their log-sum-exp.
 #include "common.hpp"
 
 namespace lsa {
 
 constexpr int kAttWGTarget = 256;   // workgroups the split heuristic aims for
 constexpr int kChunk = 32;          // attended rows per step
-constexpr int kIdxWin = 128;        // row pointers staged in LDS at a time (multiple of kChunk)
+constexpr int kMaxSplitRows = 2048; // most rows one split may take (64 chunks: one per lane)
+constexpr int kMQ = 32;             // query rows per workgroup
+constexpr int kAttRing = 4;         // ring slots of kChunk rows
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // keep the running max unless it grows by > 2^8
@@ -57,20 +58,15 @@ __device__ __forceinline__ int xcd_item(int n_items) {
     return item < n_items ? item : -1;
 }
 
-// 16-byte slot swizzle of a staged row slice (CH slots per row).  For 16- and
-// 8-slot rows it makes two access patterns conflict-free: 16 consecutive rows
-// reading one logical slot (the Q.K^T operand) and the 8 rows
-// {j, j+8 : j in 4h..4h+3} reading one slot pair (the transposing P.V reads).
-template <int CH>
+// 16-byte slot swizzle of a staged latent row (a multiple of 16 slots, so every
+// row starts on the same bank): physical slot p of row r holds logical slot
+// p ^ slot_swz(r).  Conflict-free for 16 consecutive rows reading one logical
+// slot (the Q K^T operand: the values over r mod 16 are a permutation of 0..15)
+// and for the 8 rows {j, j+8 : j in 4h..4h+3} reading one even/odd slot pair
+// (the transposing P C reads: those rows take 8 distinct values, all even or
+// all odd).
 __device__ __forceinline__ int slot_swz(int r) {
-    if constexpr (CH == 16) {
-        return 2 * ((r & 3) + 4 * ((r >> 3) & 1)) + ((r >> 2) & 1);
-    } else if constexpr (CH == 8) {
-        // two rows per 64 banks: the slot must differ among rows of equal parity
-        return (((r >> 1) & 1) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 2);
-    } else {
-        return 0;
-    }
+    return 2 * ((r & 3) + 4 * ((r >> 3) & 1)) + ((r >> 2) & 1);
 }
 
 // Reductions over RG adjacent lanes (RG in {4, 8, 16}) with DPP lane moves.
@@ -102,54 +98,67 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int NW, int DPW, int HT>
-__global__ __launch_bounds__(NW * 64, 2) void k_attend_mfma(
-    const bf16* __restrict__ qa, int T, int Hq, const bf16* __restrict__ latent,
+// Workgroup barrier for LDS traffic only: this wave's LDS operations retire
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, so the direct-to-LDS copies of later chunks stay in
+// flight across it; each wave waits for its own copies with wait_vmcnt first.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0), vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+}
+
+template <int Dl, int NB>
+__global__ __launch_bounds__(512, 1) void k_attend_mfma(
+    const bf16* __restrict__ qa, int M, const bf16* __restrict__ latent,
     const int64_t* __restrict__ latent_row_start, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ topk_count, int k, const bf16* __restrict__ hca,
     const int64_t* __restrict__ hca_row_start, const int32_t* __restrict__ hca_count,
-    int64_t max_hca, float scale_log2, int HG, int nsplit, int rows_per_split, int n_items,
+    int64_t max_hca, float scale_log2, int QG, int nsplit, int rows_per_split, int n_items,
     bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
     float* __restrict__ part_lse) {
-    constexpr int Dl = NW * DPW;
-    constexpr int KDT = DPW / 32;           // k-steps of Q.K^T over the wave's dims
-    constexpr int NDT = DPW / 16;           // 16-wide dim tiles of P.V
-    constexpr int CH = DPW / 8;             // 16-byte slots per row slice
-    constexpr int SLICE = kChunk * DPW;     // bf16 per wave per ring slot
-    constexpr int NBUF = NW >= 8 ? 3 : 4;   // ring depth (LDS: slots + partial logits <= 160 KiB)
-    constexpr int RPI = 64 / CH;            // rows per DMA instruction
-    constexpr int DMA = kChunk / RPI;       // DMA instructions per wave per chunk
-    constexpr int SROW = 36;                // floats per head row of a partial-logit tile
-    constexpr int PROW = 40;                // bf16 per head row of P
-    constexpr int MH = 16 * HT;             // query heads per workgroup
-    constexpr int HPW = MH / NW;            // heads whose softmax one wave finishes
-    constexpr int RG = 64 / HPW;            // lanes sharing one head in that softmax
-    constexpr int RPL = kChunk / RG;        // rows per lane in that softmax
-    static_assert(KDT >= 1 && (RPL == 2 || RPL == 4) && (RG == 8 || RG == 16), "tiling");
-    static_assert(DMA * NBUF < 64, "vmcnt range");
+    constexpr int NW = 4;                       // compute waves (waves 0..3)
+    constexpr int NP = 4;                       // copy waves (waves 4..7)
+    constexpr int SL = Dl / 8;                  // 16-byte slots per latent row
+    constexpr int RPI = 64 / SL;                // rows per direct-to-LDS instruction
+    constexpr int IPW = kChunk / (RPI * NP);    // such instructions per copy wave per chunk
+    constexpr int KDT = Dl / 32;                // k-steps of Q K^T
+    constexpr int DPW = Dl / NW;                // latent dims per wave in P C
+    constexpr int NDT = DPW / 16;               // 16-wide dim tiles of P C
+    constexpr int PROW = 40;                    // bf16 per query row of P (conflict-free reads)
+    static_assert(SL >= 16 && IPW >= 1 && NB >= 2 && NB <= 4, "tiling");
+    static_assert(kMQ * DPW * NW <= kChunk * Dl, "output staging fits one ring slot");
 
-    __shared__ __attribute__((aligned(16))) bf16 cring[NBUF][NW][SLICE];
-    __shared__ __attribute__((aligned(16))) float sbuf[NW][MH * SROW];
-    __shared__ __attribute__((aligned(16))) bf16 pbuf[MH * PROW];
-    __shared__ __attribute__((aligned(16))) float abuf[MH];
-    __shared__ float mlbuf[2][MH];
-    __shared__ const bf16* sptr[kIdxWin];   // row pointers of a window of this split's rows
+    // One LDS object holds every buffer: the compiler then leaves the ordering of
+    // the direct-to-LDS copies and the LDS reads to the explicit counted waits
+    // and barriers below instead of draining all copies before each LDS read.
+    constexpr int OFF_PBUF = NB * kChunk * Dl * 2;          // ring: NB slots of kChunk rows
+    constexpr int OFF_SMAX = OFF_PBUF + kMQ * PROW * 2;     // P (bf16)
+    constexpr int OFF_SSUM = OFF_SMAX + 2 * kMQ * 4;        // chunk maxima of the two row tiles
+    constexpr int OFF_ABUF = OFF_SSUM + 2 * kMQ * 4;        // and their sums of P
+    constexpr int OFF_ML = OFF_ABUF + kMQ * 4;              // rescale factors of O
+    constexpr int LDS_BYTES = OFF_ML + 2 * kMQ * 4;         // final (m, l)
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    bf16* const ring0 = reinterpret_cast<bf16*>(lds);
+    bf16* const pbuf = reinterpret_cast<bf16*>(lds + OFF_PBUF);
+    float (*const smax)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_SMAX);
+    float (*const ssum)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_SSUM);
+    float* const abuf = reinterpret_cast<float*>(lds + OFF_ABUF);
+    float (*const mlbuf)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_ML);
 
     const int item = xcd_item(n_items);
     if (item < 0) return;
-    const int hg = item % HG;
-    const int split = (item / HG) % nsplit;
-    const int64_t bt = item / (HG * nsplit);
-    const int b = (int)(bt / T);
-    const int h0 = hg * MH;
+    const int qg = item % QG;
+    const int split = (item / QG) % nsplit;
+    const int b = item / (QG * nsplit);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
     const int n16 = lane & 15;
     const int g = lane >> 4;
-    const int si = lane / RG;               // softmax: local head HPW*wave + si
-    const int sr = (lane % RG) * RPL;       // softmax: first row of this lane
+    const bool copier = wave >= NW;
+    const int rt = (wave >> 1) & 1;             // Q K^T: chunk rows 16rt .. 16rt+15
+    const int ht = wave & 1;                    //        query rows 16ht .. 16ht+15
 
     const int ntop = min(topk_count[b], k);
     const int nh = hca ? (int)min((int64_t)hca_count[b], max_hca) : 0;
@@ -159,225 +168,280 @@ __global__ __launch_bounds__(NW * 64, 2) void k_attend_mfma(
     const int64_t lrs = latent_row_start[b];
     const int64_t hrs = hca ? hca_row_start[b] : 0;
     const int32_t* idx = topk_idx + (int64_t)b * k;
-    const int dim0 = wave * DPW;
     const int nchunks = re > rs ? (re - rs + kChunk - 1) / kChunk : 0;
+    const int64_t qrow0 = (int64_t)b * M + (int64_t)qg * kMQ;   // first query row of the group
+    const int mq = min(kMQ, M - qg * kMQ);                        // valid query rows
 
-    // Q fragments: A operand, heads h0 + 16ht + n16, dims dim0 + 32kk + 8g.
-    bf16x8 qf[HT][KDT];
+    // Q fragments (A operand): query row 16ht + n16, dims 32kk + 8g .. +7
+    bf16x8 qf[KDT];
+    if (!copier) {
+        const bool ok = 16 * ht + n16 < mq;
+        const bf16* qp = qa + (qrow0 + (ok ? 16 * ht + n16 : 0)) * Dl + 8 * g;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int h = h0 + 16 * ht + n16;
-#pragma unroll
-        for (int kk = 0; kk < KDT; ++kk)
-            qf[ht][kk] = h < Hq ? load8(qa + (bt * Hq + h) * Dl + dim0 + 32 * kk + 8 * g) : zero8();
+        for (int kk = 0; kk < KDT; ++kk) qf[kk] = ok ? load8(qp + 32 * kk) : zero8();
     }
-    f32x4 o[HT][NDT];
+    // Copy wave p stages rows 8p .. 8p+7 of every chunk.  Lane c holds the
+    // chosen-entry indices of those rows of chunk c (a split has at most 64
+    // chunks); rows past the split end are clamped to its last row.
+    // The loads are speculative (clamped into the index row, used only for rows
+    // below the top-k count), so they do not wait for the counts; rows past the
+    // split end re-read the split's first row.
+    int ridx[8];
+    int first_idx = 0;
+    if (copier) {
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+        for (int j8 = 0; j8 < 8; ++j8)
+            ridx[j8] = idx[min(rs + kChunk * lane + 8 * (wave - NW) + j8, k - 1)];
+        first_idx = idx[min(rs, k - 1)];
+    }
+    // Q (compute waves) and the indices (copy waves) are complete before the
+    // loop.  Only the copy waves issue copies, so their counted waits below are
+    // exact, and the compute waves never have a copy outstanding when they read
+    // LDS.
+    wait_vmcnt<0>();
+    f32x4 o[2][NDT];
 #pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) o[ht][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_ref = -INFINITY;   // running max (base 2) of local head HPW*wave + si
-    float l_run = 0.0f;
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) o[h2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // running max (base 2) and sum of query rows 16ht + 4g + v (sums kept by rt == 0)
+    float m_ref[4], l_run[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        m_ref[v] = -INFINITY;
+        l_run[v] = 0.0f;
+    }
 
-    // Row pointers of rows [win0, win0 + kIdxWin) staged in LDS; rows past the
-    // split end point at its last row (finite data, probability zero).
-    int win0 = -kIdxWin;
-    auto stage_window = [&](int w0) {
-        __syncthreads();
-        for (int i = tid; i < kIdxWin; i += NW * 64) {
-            const int j = min(w0 + i, re - 1);
-            sptr[i] = j < ntop ? latent + (lrs + idx[j]) * Dl : hca + (hrs + (j - ntop)) * Dl;
-        }
-        __syncthreads();
-        win0 = w0;
-    };
-    // DMA of this wave's slice of chunk c into ring slot c % NBUF: instruction i
-    // moves rows RPI*i .. RPI*i+RPI-1, lane L filling physical slot L % CH of row
-    // RPI*i + L / CH with logical slot (L % CH) ^ swz(row).
+    // Chunk c -> ring slot c % NB.  Instruction i of copy wave p moves chunk rows
+    // 8p + RPI*i ..; lane L fills physical slot L % SL of its row r with logical
+    // slot (L % SL) ^ swz(r).  Rows past the split end re-read its first row
+    // (finite data, probability zero).
     auto issue_chunk = [&](int c) {
         const int r0 = rs + c * kChunk;
-        if (min(r0 + kChunk, re) > win0 + kIdxWin) stage_window(r0);
-        bf16* slot = &cring[c % NBUF][wave][0];
+        bf16* slot = ring0 + (c % NB) * (kChunk * Dl);
 #pragma unroll
-        for (int i = 0; i < DMA; ++i) {
-            const int rl = RPI * i + lane / CH;
-            const int ps = lane % CH;
-            const bf16* src = sptr[min(r0 + rl, re - 1) - win0] + dim0 + 8 * (ps ^ slot_swz<CH>(rl));
+        for (int i = 0; i < IPW; ++i) {
+            const int sub = lane / SL;                     // row of this lane in the instruction
+            const int rbase = 8 * (wave - NW) + RPI * i;
+            const int rl = rbase + sub;
+            int e = __builtin_amdgcn_readlane(ridx[RPI * i], c);
+#pragma unroll
+            for (int s2 = 1; s2 < RPI; ++s2)
+                if (sub == s2) e = __builtin_amdgcn_readlane(ridx[RPI * i + s2], c);
+            int j = r0 + rl;
+            if (j >= re) {
+                j = rs;
+                e = first_idx;
+            }
+            const bf16* row = j < ntop ? latent + (lrs + e) * Dl : hca + (hrs + (j - ntop)) * Dl;
             __builtin_amdgcn_global_load_lds(
-                (const void*)src, (__attribute__((address_space(3))) void*)(slot + RPI * i * DPW),
-                16, 0, 0);
+                (const void*)(row + 8 * ((lane % SL) ^ slot_swz(rl))),
+                (__attribute__((address_space(3))) void*)(slot + rbase * Dl), 16, 0, 0);
         }
     };
 
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     auto process = [&](int c) {
         const int r0 = rs + c * kChunk;
-        const bf16* slot = &cring[c % NBUF][wave][0];
-        // partial logits over this wave's dims; B operands from the staged slice
-        f32x4 sp[HT][2];
+        const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
+        // S tile: D[4g+v][n16] = query row 16ht + 4g + v against chunk row 16rt + n16
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            const int r = 16 * rt + n16;
+            const bf16* rp = sl + r * Dl;
+            const int sw = slot_swz(r);
+            // K operands through an 8-deep register window: 8 reads stay in flight
+            constexpr int KW = KDT < 8 ? KDT : 8;
+            bf16x8 kb[KW];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) sp[ht][c2] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-            const int r = 16 * c2 + n16;
-            const int sw = slot_swz<CH>(r);
+            for (int kk = 0; kk < KW; ++kk)
+                kb[kk] = *reinterpret_cast<const bf16x8*>(rp + 8 * ((4 * kk + g) ^ sw));
 #pragma unroll
             for (int kk = 0; kk < KDT; ++kk) {
-                const bf16x8 kb = *reinterpret_cast<const bf16x8*>(slot + r * DPW + 8 * ((4 * kk + g) ^ sw));
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) sp[ht][c2] = mfma16(qf[ht][kk], kb, sp[ht][c2]);
+                sacc = mfma16(qf[kk], kb[kk % KW], sacc);
+                if (kk + KW < KDT)
+                    kb[kk % KW] = *reinterpret_cast<const bf16x8*>(rp + 8 * ((4 * (kk + KW) + g) ^ sw));
             }
+            // schedule: the first KW reads, then one product per refill read
+            __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);
+#pragma unroll
+            for (int kk = 0; kk < KDT - KW; ++kk) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, KW, 0);
         }
-        float* swb = sbuf[wave];
+        // this lane holds query rows q0 + v (v = 0..3) against chunk row 16rt + n16
+        const int q0 = 16 * ht + 4 * g;
+        const bool valid = r0 + 16 * rt + n16 < re;
+        f32x4 x, cm;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int v = 0; v < 4; ++v) x[v] = valid ? sacc[v] * scale_log2 : -INFINITY;
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2)
+        for (int v = 0; v < 4; ++v) cm[v] = group_max<16>(x[v]);
+        if (n16 == 0) *reinterpret_cast<f32x4*>(&smax[rt][q0]) = cm;
+        lds_barrier();
+        const f32x4 ma = *reinterpret_cast<const f32x4*>(&smax[0][q0]);
+        const f32x4 mb = *reinterpret_cast<const f32x4*>(&smax[1][q0]);
+        // Lazy rescale, branch-free: the running max moves only when the chunk max
+        // exceeds it by more than kRescaleSlack (always on the first chunk, as
+        // -inf + slack = -inf); then alpha = 2^(m_old - m_new), 0 on the first
+        // chunk.  x - m_ref <= kRescaleSlack afterwards, so p <= 2^kRescaleSlack.
+        f32x4 alpha, ps;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) swb[(16 * ht + 4 * g + v) * SROW + 16 * c2 + n16] = sp[ht][c2][v];
-        __syncthreads();
-
-        // softmax of local head HPW*wave + si over rows sr .. sr+3 of this chunk
-        {
-            const int h = HPW * wave + si;
-            float x[RPL];
-#pragma unroll
-            for (int j = 0; j < RPL; ++j) x[j] = 0.0f;
-#pragma unroll
-            for (int w2 = 0; w2 < NW; ++w2) {
-                if constexpr (RPL == 4) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(&sbuf[w2][h * SROW + sr]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) x[j] += a[j];
-                } else {
-                    const float2 a = *reinterpret_cast<const float2*>(&sbuf[w2][h * SROW + sr]);
-                    x[0] += a.x;
-                    x[1] += a.y;
-                }
-            }
-            float cmax = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < RPL; ++j) {
-                x[j] = (r0 + sr + j < re) ? x[j] * scale_log2 : -INFINITY;
-                cmax = fmaxf(cmax, x[j]);
-            }
-            cmax = group_max<RG>(cmax);
-            float alpha = 1.0f;
-            if (cmax > m_ref + kRescaleSlack || (m_ref == -INFINITY && cmax != -INFINITY)) {
-                alpha = (m_ref == -INFINITY) ? 0.0f : exp2f(m_ref - cmax);
-                m_ref = cmax;
-            }
-            float psum = 0.0f;
-            typedef __bf16 bf16xR __attribute__((ext_vector_type(RPL)));
-            bf16xR pv;
-#pragma unroll
-            for (int j = 0; j < RPL; ++j) {
-                const float p = (m_ref == -INFINITY) ? 0.0f : exp2f(x[j] - m_ref);
-                pv[j] = (bf16)p;
-                psum += (float)pv[j];
-            }
-            psum = group_sum<RG>(psum);
-            l_run = alpha * l_run + psum;
-            *reinterpret_cast<bf16xR*>(&pbuf[h * PROW + sr]) = pv;
-            if (sr == 0) abuf[h] = alpha;
+        for (int v = 0; v < 4; ++v) {
+            const float cmax = fmaxf(ma[v], mb[v]);
+            const bool grow = cmax > m_ref[v] + kRescaleSlack;
+            alpha[v] = grow ? __builtin_amdgcn_exp2f(m_ref[v] - cmax) : 1.0f;
+            m_ref[v] = grow ? cmax : m_ref[v];
+            const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
+            const bf16 pb = (bf16)p;
+            pbuf[(q0 + v) * PROW + 16 * rt + n16] = pb;
+            ps[v] = (float)pb;
         }
-        __syncthreads();
-
-        // rescale O rows whose head max moved
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * ht + 4 * g]);
+        for (int v = 0; v < 4; ++v) ps[v] = group_sum<16>(ps[v]);
+        if (n16 == 0) {
+            *reinterpret_cast<f32x4*>(&ssum[rt][q0]) = ps;
+            if (rt == 0) *reinterpret_cast<f32x4*>(&abuf[q0]) = alpha;
+        }
+        lds_barrier();
+        if (rt == 0) {
+            const f32x4 sa = *reinterpret_cast<const f32x4*>(&ssum[0][q0]);
+            const f32x4 sb = *reinterpret_cast<const f32x4*>(&ssum[1][q0]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) l_run[v] = alpha[v] * l_run[v] + (sa[v] + sb[v]);
+        }
+        // rescale O rows whose running max moved
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * h2 + 4 * g]);
             if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {
 #pragma unroll
                 for (int nt = 0; nt < NDT; ++nt)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) o[ht][nt][v] *= al[v];
+                    for (int v = 0; v < 4; ++v) o[h2][nt][v] *= al[v];
             }
         }
-        // O[:, dims_w] += P . C[:, dims_w]; C^T operands come from transposing LDS reads:
-        // in each 16-lane group, lanes 4j..4j+3 point at row (8g + j) (4 dims each) and
-        // lane i receives dim i of those 4 rows.
-        bf16x8 pa[HT];
+        // P C over this wave's dims.  A: query row 16h2 + n16, chunk rows 8g .. 8g+7.
+        // B from transposing reads: in each 16-lane group, lanes 4j..4j+3 point at
+        // chunk row 8g + j (+4 for the upper half), 4 dims each, and lane i receives
+        // dim i of those 4 rows.
+        bf16x8 pa[2];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-            pa[ht] = *reinterpret_cast<const bf16x8*>(&pbuf[(16 * ht + n16) * PROW + 8 * g]);
+        for (int h2 = 0; h2 < 2; ++h2)
+            pa[h2] = *reinterpret_cast<const bf16x8*>(&pbuf[(16 * h2 + n16) * PROW + 8 * g]);
         const int trow0 = 8 * g + (n16 >> 2);
         const int trow1 = trow0 + 4;
-        const int sw0 = slot_swz<CH>(trow0), sw1 = slot_swz<CH>(trow1);
+        const int sw0 = slot_swz(trow0), sw1 = slot_swz(trow1);
         const int q4 = n16 & 3;
+        const int off = 4 * (q4 & 1);
+        // all of the chunk's C^T operands are read before the products, so the
+        // transposing reads overlap each other rather than the matrix ops
+        bf16x4 lo[NDT], hi[NDT];
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) {
-            const int ls = 2 * nt + (q4 >> 1);       // logical 16-byte slot
-            const int off = 4 * (q4 & 1);            // bf16 offset inside the slot
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(slot + trow0 * DPW + 8 * (ls ^ sw0) + off));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (__attribute__((address_space(3))) bf16x4*)(slot + trow1 * DPW + 8 * (ls ^ sw1) + off));
+            const int ls = (DPW / 8) * wave + 2 * nt + (q4 >> 1);   // logical 16-byte slot
+            lo[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(sl + trow0 * Dl + 8 * (ls ^ sw0) + off));
+            hi[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(sl + trow1 * Dl + 8 * (ls ^ sw1) + off));
+        }
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) {
             bf16x8 cb;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                cb[j] = lo[j];
-                cb[4 + j] = hi[j];
+                cb[j] = lo[nt][j];
+                cb[4 + j] = hi[nt][j];
             }
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) o[ht][nt] = mfma16(pa[ht], cb, o[ht][nt]);
+            for (int h2 = 0; h2 < 2; ++h2) o[h2][nt] = mfma16(pa[h2], cb, o[h2][nt]);
         }
+        // schedule: every LDS read of P and C^T first, then the products
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NDT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);
     };
 
-    // Pipeline: chunks c+1 .. c+NBUF-1 are in flight while chunk c is processed.
+    // Pipeline: the copy waves keep NB-1 chunks staged ahead of the compute
+    // waves.  Three barriers per chunk, taken by all eight waves: B0 (chunk c is
+    // in LDS; every read of chunk c-1 has retired, so its slot is refilled right
+    // after) and the two inside process(c).
+    if (copier) {
 #pragma unroll
-    for (int c = 0; c < NBUF - 1; ++c)
-        if (c < nchunks) issue_chunk(c);
+        for (int c = 0; c < NB - 1; ++c)
+            if (c < nchunks) issue_chunk(c);
+        for (int c = 0; c < nchunks; ++c) {
+            const int after = min(nchunks - 1, c + NB - 2) - c;   // chunks issued after c
+            if (after >= 2) wait_vmcnt<2 * IPW>();
+            else if (after == 1) wait_vmcnt<IPW>();
+            else wait_vmcnt<0>();
+            static_assert(NB <= 4, "the waits above cover two later chunks");
+            lds_barrier();
+            if (c + NB - 1 < nchunks) issue_chunk(c + NB - 1);
+            lds_barrier();
+            lds_barrier();
+        }
+        // the two barriers of the output stage below
+        lds_barrier();
+        lds_barrier();
+        return;
+    }
     for (int c = 0; c < nchunks; ++c) {
-        // refill the slot of chunk c-1 (its last reads were in the previous step)
-        // before waiting, so the address work overlaps the wait and Q.K^T
-        if (c + NBUF - 1 < nchunks) issue_chunk(c + NBUF - 1);
-        const int after = min(nchunks - 1, c + NBUF - 1) - c;   // chunks issued after c
-        if (after >= 3) wait_vmcnt<3 * DMA>();
-        else if (after == 2) wait_vmcnt<2 * DMA>();
-        else if (after == 1) wait_vmcnt<DMA>();
-        else wait_vmcnt<0>();
+        lds_barrier();
         process(c);
     }
 
-    // publish (m, l) of this wave's heads; every wave normalises its O rows
-    if (sr == 0) {
-        mlbuf[0][HPW * wave + si] = m_ref;
-        mlbuf[1][HPW * wave + si] = l_run;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+    // publish (m, l); every wave normalises its O columns and stages them in LDS
+    // (ring slot 0, free now) so the stores to HBM are 16 bytes per lane
+    if (rt == 0 && n16 == 0) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int hl = 16 * ht + 4 * g + v;
-            const int h = h0 + hl;
-            if (h >= Hq) continue;
-            const float l = mlbuf[1][hl];
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-            bf16* orow = (nsplit == 1) ? out + (bt * Hq + h) * Dl + dim0
-                                       : part_o + ((bt * nsplit + split) * Hq + h) * Dl + dim0;
-#pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) orow[16 * nt + n16] = (bf16)(o[ht][nt][v] * inv);
+            mlbuf[0][16 * ht + 4 * g + v] = m_ref[v];
+            mlbuf[1][16 * ht + 4 * g + v] = l_run[v];
         }
-    if (tid < MH) {
-        const int h = h0 + tid;
-        if (h < Hq) {
-            const float l = mlbuf[1][tid];
-            const float v = l > 0.0f ? (mlbuf[0][tid] + log2f(l)) * kLn2 : -INFINITY;
-            if (nsplit == 1) {
-                if (lse) lse[bt * Hq + h] = v;
-            } else {
-                part_lse[(bt * nsplit + split) * Hq + h] = v;
-            }
+    }
+    lds_barrier();
+    bf16* ost = ring0 + wave * (kMQ * DPW);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int ql = 16 * h2 + 4 * g + v;
+            const float l = mlbuf[1][ql];
+            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < NDT; ++nt) ost[ql * DPW + 16 * nt + n16] = (bf16)(o[h2][nt][v] * inv);
+        }
+    lds_barrier();
+    {
+        constexpr int LPR = DPW / 8;            // lanes per staged query row
+        constexpr int RPS = 64 / LPR;           // query rows per store step
+        bf16* dst_base = (nsplit == 1) ? out + qrow0 * Dl
+                                       : part_o + ((int64_t)(b * nsplit + split) * M +
+                                                   (int64_t)qg * kMQ) * Dl;
+#pragma unroll
+        for (int i = 0; i < kMQ / RPS; ++i) {
+            const int ql = RPS * i + lane / LPR;
+            const int c8 = 8 * (lane % LPR);
+            if (ql < mq)
+                *reinterpret_cast<bf16x8*>(dst_base + (int64_t)ql * Dl + DPW * wave + c8) =
+                    *reinterpret_cast<const bf16x8*>(ost + ql * DPW + c8);
+        }
+    }
+    if (tid < mq) {
+        const float l = mlbuf[1][tid];
+        const float v = l > 0.0f ? (mlbuf[0][tid] + log2f(l)) * kLn2 : -INFINITY;
+        if (nsplit == 1) {
+            if (lse) lse[qrow0 + tid] = v;
+        } else {
+            part_lse[(int64_t)(b * nsplit + split) * M + (int64_t)qg * kMQ + tid] = v;
         }
     }
 }
 
 // Merge the split partials: o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M) per
-// (b, t, h); the partial o_s are normalised per split and stored in bf16.
+// query row; the partial o_s are normalised per split and stored in bf16.
 // A workgroup of 256 threads merges 4 heads; each thread owns 8 dims (16-byte loads).
 constexpr int kCombHeads = 4;
 
@@ -498,13 +562,11 @@ __global__ __launch_bounds__(256) void k_attend_vector(
     if (threadIdx.x == 0 && lse) lse[bt * Hq + h] = l > 0.0f ? m + logf(l) : -INFINITY;
 }
 
-// Split heuristic shared by the launch and the workspace query: head groups of
-// kMH heads, then enough row splits to give ~kAttWGTarget workgroups, keeping
+// Split heuristic shared by the launch and the workspace query: groups of kMQ
+// query rows, then enough row splits to give ~kAttWGTarget workgroups, keeping
 // at least two row chunks per split.
-constexpr int kMH = 32;
-
 struct AttendPlan {
-    int HG;
+    int QG;
     int nsplit;
     int rows_per_split;
     int n_items;
@@ -512,8 +574,9 @@ struct AttendPlan {
 
 static AttendPlan attend_plan(int B, int T, int Hq, int k, int64_t max_hca) {
     const int64_t rows = (int64_t)k + (max_hca > 0 ? max_hca : 0);
-    const int HG = (Hq + kMH - 1) / kMH;
-    const int64_t units = (int64_t)B * T * HG;
+    const int64_t M = (int64_t)T * Hq;
+    const int QG = (int)((M + kMQ - 1) / kMQ);
+    const int64_t units = (int64_t)B * QG;
     int64_t ns = (kAttWGTarget + units - 1) / units;
     const int64_t max_ns = (rows + 2 * kChunk - 1) / (2 * kChunk);
     if (ns > max_ns) ns = max_ns;
@@ -521,13 +584,15 @@ static AttendPlan attend_plan(int B, int T, int Hq, int k, int64_t max_hca) {
     int64_t rps = (rows + ns - 1) / ns;
     rps = (rps + kChunk - 1) / kChunk * kChunk;
     if (rps < kChunk) rps = kChunk;
+    if (rps > kMaxSplitRows) rps = kMaxSplitRows;
     ns = (rows + rps - 1) / rps;
     if (ns < 1) ns = 1;
-    return AttendPlan{HG, (int)ns, (int)rps, (int)(units * ns)};
+    return AttendPlan{QG, (int)ns, (int)rps, (int)(units * ns)};
 }
 
 static bool attend_mfma_shape(int dtype, int Hq, int Dl) {
-    return dtype == LSA_DTYPE_BF16 && Hq <= 64 && (Dl == 128 || Dl == 256 || Dl == 512);
+    (void)Hq;
+    return dtype == LSA_DTYPE_BF16 && (Dl == 128 || Dl == 256 || Dl == 512);
 }
 
 }  // namespace lsa
@@ -583,20 +648,22 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
         float* part_lse = p.nsplit > 1 ? (float*)(part_o + n * Dl) : nullptr;
         const unsigned grid = (unsigned)(8 * ((p.n_items + 7) / 8));
         const float sl2 = scale * kLog2e;
-#define LSA_ATT(nw, dpw)                                                                        \
-    hipLaunchKernelGGL((k_attend_mfma<nw, dpw, kMH / 16>), dim3(grid), dim3(nw * 64), 0, st,      \
-                       (const bf16*)qa, T, Hq, (const bf16*)latent, latent_row_start, topk_idx,  \
-                       topk_count, k, (const bf16*)hca, hca_row_start, hca_count, hmax, sl2,     \
-                       p.HG, p.nsplit, p.rows_per_split, p.n_items, (bf16*)out, lse, part_o,     \
+        const int M = T * Hq;
+#define LSA_ATT(dl)                                                                            \
+    hipLaunchKernelGGL((k_attend_mfma<dl, kAttRing>), dim3(grid), dim3(512), 0, st,             \
+                       (const bf16*)qa, M, (const bf16*)latent, latent_row_start, topk_idx,     \
+                       topk_count, k, (const bf16*)hca, hca_row_start, hca_count, hmax, sl2,    \
+                       p.QG, p.nsplit, p.rows_per_split, p.n_items, (bf16*)out, lse, part_o,    \
                        part_lse)
-        if (Dl == 512) LSA_ATT(8, 64); else if (Dl == 256) LSA_ATT(4, 64); else LSA_ATT(4, 32);
+        if (Dl == 512) LSA_ATT(512); else if (Dl == 256) LSA_ATT(256); else LSA_ATT(128);
 #undef LSA_ATT
         rc = launch_status("attend_mfma");
         if (rc != LSA_OK || p.nsplit == 1) return rc;
-        const int64_t nbh = (int64_t)B * T * Hq;
+        // partials are laid out [b][split][query row]: merge with M = T * Hq rows per b
+        const int64_t nbh = (int64_t)B * M;
         hipLaunchKernelGGL(k_attend_combine<bf16>,
                            dim3((unsigned)((nbh + kCombHeads - 1) / kCombHeads)), dim3(256),
-                           sizeof(float) * kCombHeads * p.nsplit, st, Hq, Dl, p.nsplit, nbh,
+                           sizeof(float) * kCombHeads * p.nsplit, st, M, Dl, p.nsplit, nbh,
                            part_o, part_lse, (bf16*)out, lse);
         return launch_status("attend_combine");
     }
