@@ -7,21 +7,36 @@
 // index, NaN last, -0.0 == +0.0.  The kept set is returned in ascending index.
 //
 // One workgroup (1024 threads) per sequence.  Keys are mapped to
-// order-preserving uint32, staged in LDS (up to kCap candidates; larger sets
-// use a global scratch area), and a radix select over 8-bit digits -- starting
-// below the bits every candidate shares -- finds the k-th key U and how many
-// keys equal to U to take.  A last ordered pass
-// keeps every key > U and the first `need` keys == U (the smallest indices,
-// since candidates are in ascending order), compacted with workgroup scans.
+// order-preserving uint32.  The k-th largest key U is found digit by digit,
+// most significant first; the keys sharing the digits fixed so far shrink with
+// every step, and once at most kShort remain they are copied to a short list,
+// once at most kRank remain they are ranked exactly (count of larger and of
+// equal keys).  A last ordered pass keeps every key > U and the first `need`
+// keys == U (the smallest indices: candidates arrive in ascending order).
+//
+//   n <= kRegCap: every candidate stays in registers from the gather to the
+//     output (wave w holds a contiguous run of 64-candidate chunks, key and
+//     index); the first digit is the fixed top 12 bits (sign, exponent, 3
+//     mantissa bits), histogrammed during the gather; the ordered pass uses
+//     ballots per chunk and one scan over the 16 waves.
+//   n >  kRegCap: keys in a global scratch area; 8-bit digits starting below
+//     the bits every candidate shares; the ordered pass walks per-thread runs.
 #include "common.hpp"
 
 namespace lsa {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kCap = 32768;                      // candidates held in LDS
-constexpr int kCapPadded = kCap + kCap / 32;     // one pad word per 32 (bank spread)
-constexpr int kHistCopies = 16;                  // lane-spread copies of each radix bin
+constexpr int kRunChunks = 32;                   // 64-candidate chunks per wave held in registers
+constexpr int kRegCap = kTkWaves * kRunChunks * kWave;  // 32768 candidates
+constexpr int kHistCopies = 16;                  // lane-spread copies of each 8-bit radix bin
+constexpr int kShort = 2048;                     // longest digit list copied to the short list
+constexpr int kRank = 256;                       // longest list ranked by direct counting
+constexpr int kD0 = 12;                          // first digit of the register path (bits 31..20)
+constexpr int kBins0 = 1 << kD0;
+constexpr int kCopies0 = 8;                      // lane-spread copies of each first-digit bin
+constexpr int kHistWords = kBins0 * kCopies0;    // 128 KiB; the 8-bit passes use the first 4096
+static_assert(kBins0 == 4 * kTkThreads && 256 * kHistCopies <= kHistWords, "histogram layout");
 
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
@@ -53,15 +68,333 @@ __device__ __forceinline__ int block_excl_scan(int x, int* scratch, int* total) 
     return pre + incl - x;
 }
 
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Search state: the need-th largest key among those with (key & pmask) == prefix
+// is the k-th key overall; m keys match; bits below hi are still open.
+struct RadixState {
+    uint32_t prefix, pmask;
+    int hi, m, need;
+};
+
+// Narrow the search until every bit is fixed (prefix = U, need = how many keys
+// equal to U to take).  Workgroup-wide; hist holds >= 256 * kHistCopies words.
+// Global-path refinement over keys[0..n) (IN_LDS selects the padded LDS layout):
+// narrow the search until every bit is fixed (prefix = U, need = how many keys
+// equal to U to take).  Workgroup-wide; hist holds >= 256 * kHistCopies words.
 template <bool IN_LDS>
-__device__ void topk_body(const float* __restrict__ rb, const int32_t* __restrict__ cand, int n,
-                          int k, uint32_t* keys, int32_t* __restrict__ out, unsigned* hist,
+__device__ void radix_refine(const uint32_t* keys, int n, RadixState& st, unsigned* hist,
+                             uint32_t* shortl, int* sh);
+
+// The 8-bit digit search shared by both refinements: lane l of wave 0 owns
+// digits 4l..4l+3 of the histogram; writes (digit, need within it, its count).
+__device__ __forceinline__ void digit_search(const unsigned* hist, int need, int* sh) {
+    const int tid = threadIdx.x;
+    int c4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u32x4* hq = reinterpret_cast<const u32x4*>(&hist[(4 * tid + q) * kHistCopies]);
+        int t = 0;
+#pragma unroll
+        for (int i = 0; i < kHistCopies / 4; ++i) {
+            const u32x4 v = hq[i];
+            t += (int)(v[0] + v[1] + v[2] + v[3]);
+        }
+        c4[q] = t;
+    }
+    const int tot = c4[0] + c4[1] + c4[2] + c4[3];
+    int suf = tot;  // inclusive suffix sum over lanes >= tid
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_down(suf, off);
+        if (tid + off < 64) suf += y;
+    }
+    const int above = suf - tot;  // keys with a digit in higher lanes
+    if (above < need && need <= suf) {
+        int acc = above, q = 3;
+        for (; q > 0; --q) {
+            if (acc + c4[q] >= need) break;
+            acc += c4[q];
+        }
+        sh[0] = 4 * tid + q;
+        sh[1] = need - acc;
+        sh[2] = c4[q];
+    }
+}
+
+// Exact rank of the k-th key among the m keys in list[0..m): the key with
+// (#larger) < need <= (#larger + #equal); every thread holding such a key writes
+// the same answer to sh[4], sh[5].
+__device__ __forceinline__ void rank_list(const uint32_t* list, int m, int need, int* sh) {
+    const int tid = threadIdx.x;
+    if (tid < m) {
+        const uint32_t x = list[tid];
+        int gt = 0, eq = 0;
+        for (int i = 0; i < (m & ~3); i += 4) {
+            const u32x4 y = *reinterpret_cast<const u32x4*>(&list[i]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                gt += y[e] > x;
+                eq += y[e] == x;
+            }
+        }
+        for (int i = m & ~3; i < m; ++i) {
+            gt += list[i] > x;
+            eq += list[i] == x;
+        }
+        if (gt < need && need <= gt + eq) {
+            sh[4] = (int)x;
+            sh[5] = need - gt;
+        }
+    }
+}
+
+// n <= kRegCap: candidates in registers.  Wave w holds chunks [w*cpw, (w+1)*cpw)
+// of 64 consecutive candidates; lane l of chunk u is candidate (w*cpw + u)*64 + l.
+__device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restrict__ cand, int n,
+                          int k, int32_t* __restrict__ out, unsigned* hist, uint32_t* shortl,
                           int* scratch, int* sh) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int cpw = (n + kTkWaves * kWave - 1) / (kTkWaves * kWave);
+    const int wb = wave * cpw * kWave;
+    uint32_t kr[kRunChunks];
+    int cr[kRunChunks];
+    // gather: candidate indices, then their keys (every load of the run in flight);
+    // the histogram is cleared meanwhile
+#pragma unroll
+    for (int u = 0; u < kRunChunks; ++u) {
+        cr[u] = 0;
+        if (u < cpw) cr[u] = cand[min(wb + kWave * u + lane, n - 1)];
+    }
+    for (int i = tid; i < kHistWords / 4; i += kTkThreads)
+        reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
+    float v[kRunChunks];
+#pragma unroll
+    for (int u = 0; u < kRunChunks; ++u) {
+        v[u] = 0.0f;
+        if (u < cpw) v[u] = rb[cr[u]];
+    }
+    __syncthreads();                                       // histogram cleared
+    const int copy = lane & (kCopies0 - 1);
+#pragma unroll
+    for (int u = 0; u < kRunChunks; ++u) {
+        kr[u] = 0u;
+        if (u < cpw) {
+            const bool in = wb + kWave * u + lane < n;
+            kr[u] = in ? order_key(v[u]) : 0u;
+            if (in) atomicAdd(&hist[(kr[u] >> (32 - kD0)) * kCopies0 + copy], 1u);
+        }
+    }
+    auto valid = [&](int u) { return u < cpw && wb + kWave * u + lane < n; };
+    __syncthreads();
+    // First digit: thread t owns bins 4(1023-t) .. +3, so the exclusive scan over
+    // threads counts the keys in higher bins.
+    {
+        const int bb = 4 * (kTkThreads - 1 - tid);
+        int c4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4* hq = reinterpret_cast<const u32x4*>(&hist[(bb + q) * kCopies0]);
+            const u32x4 a = hq[0], c = hq[1];
+            c4[q] = (int)(a[0] + a[1] + a[2] + a[3] + c[0] + c[1] + c[2] + c[3]);
+        }
+        const int tot4 = c4[0] + c4[1] + c4[2] + c4[3];
+        int total;
+        const int above = block_excl_scan(tot4, scratch, &total);
+        if (above < k && k <= above + tot4) {
+            int acc = above, q = 3;
+            for (; q > 0; --q) {
+                if (acc + c4[q] >= k) break;
+                acc += c4[q];
+            }
+            sh[0] = bb + q;
+            sh[1] = k - acc;
+            sh[2] = c4[q];
+        }
+    }
+    __syncthreads();
+    uint32_t prefix = (uint32_t)sh[0] << (32 - kD0);
+    uint32_t pmask = ~0u << (32 - kD0);
+    int hi = 32 - kD0, m = sh[2], need = sh[1];
+
+    // Refine until every bit of U is fixed.
+    bool in_short = false;
+    while (hi > 0) {
+        if (m <= kRank) {
+            // gather the m matching keys into the (free) histogram area and rank them
+            __syncthreads();                               // hist and sh are free
+            if (tid == 0) sh[3] = 0;
+            __syncthreads();
+            if (in_short) {
+                for (int j = tid; j < sh[6]; j += kTkThreads) {
+                    const uint32_t x = shortl[j];
+                    if ((x & pmask) == prefix) hist[atomicAdd(&sh[3], 1)] = x;
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < kRunChunks; ++u)
+                    if (valid(u) && (kr[u] & pmask) == prefix) hist[atomicAdd(&sh[3], 1)] = kr[u];
+            }
+            __syncthreads();
+            rank_list(hist, m, need, sh);
+            __syncthreads();
+            prefix = (uint32_t)sh[4];
+            need = sh[5];
+            break;
+        }
+        if (!in_short && m <= kShort) {
+            // copy the matching keys (any order) to the short list; later steps scan it
+            __syncthreads();                               // every thread has read sh
+            if (tid == 0) sh[3] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < kRunChunks; ++u)
+                if (valid(u) && (kr[u] & pmask) == prefix) shortl[atomicAdd(&sh[3], 1)] = kr[u];
+            __syncthreads();
+            if (tid == 0) sh[6] = sh[3];                   // list length
+            in_short = true;
+        }
+        // one pass over the next (up to) 8 bits
+        const int lo = max(hi - 8, 0);
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        __syncthreads();                                   // previous step done with hist/sh
+        for (int i = tid; i < 256 * kHistCopies; i += kTkThreads) hist[i] = 0;
+        __syncthreads();
+        const int hcopy = tid & (kHistCopies - 1);
+        if (in_short) {
+            for (int j = tid; j < sh[6]; j += kTkThreads) {
+                const uint32_t x = shortl[j];
+                if ((x & pmask) == prefix) atomicAdd(&hist[((x >> lo) & dmask) * kHistCopies + hcopy], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kRunChunks; ++u)
+                if (valid(u) && (kr[u] & pmask) == prefix)
+                    atomicAdd(&hist[((kr[u] >> lo) & dmask) * kHistCopies + hcopy], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) digit_search(hist, need, sh);
+        __syncthreads();
+        prefix |= (uint32_t)sh[0] << lo;
+        pmask |= dmask << lo;
+        need = sh[1];
+        m = sh[2];
+        hi = lo;
+    }
+    const uint32_t U = prefix;
+
+    // Ordered compaction: counts per wave by ballots, one scan over the waves,
+    // then every chunk writes its selected candidates contiguously.
+    int gt_w = 0, eq_w = 0;
+#pragma unroll
+    for (int u = 0; u < kRunChunks; ++u) {
+        if (u < cpw) {
+            const bool in = valid(u);
+            gt_w += __popcll(__ballot(in && kr[u] > U));
+            eq_w += __popcll(__ballot(in && kr[u] == U));
+        }
+    }
+    __syncthreads();                                       // scratch and sh are free
+    if (lane == 0) {
+        scratch[wave] = gt_w;
+        scratch[kTkWaves + wave] = eq_w;
+    }
+    __syncthreads();
+    int pos = 0, eqs = 0;                                  // output slot and equal keys before this wave
+    for (int w2 = 0; w2 < wave; ++w2) {
+        const int e2 = scratch[kTkWaves + w2];
+        pos += scratch[w2] + max(0, min(need - eqs, e2));
+        eqs += e2;
+    }
+#pragma unroll
+    for (int u = 0; u < kRunChunks; ++u) {
+        if (u < cpw) {                                     // uniform
+            const bool in = valid(u);
+            const bool g = in && kr[u] > U;
+            const bool e = in && kr[u] == U;
+            const uint64_t be = __ballot(e);
+            const bool sel = g || (e && eqs + lanes_below(be) < need);
+            const uint64_t bs = __ballot(sel);
+            if (sel) out[pos + lanes_below(bs)] = cr[u];
+            pos += __popcll(bs);
+            eqs += __popcll(be);
+        }
+    }
+}
+
+template <bool IN_LDS>
+__device__ void radix_refine(const uint32_t* keys, int n, RadixState& st, unsigned* hist,
+                             uint32_t* shortl, int* sh) {
     auto P = [](int j) { return IN_LDS ? j + (j >> 5) : j; };
     const int tid = threadIdx.x;
-    // Gather the keys, 8 independent loads in flight per thread (indices are
-    // clamped instead of branched on, so no load waits for the previous one).
-    // The AND and OR of all keys give the bits every candidate shares.
+    bool in_short = false;
+    int cnt = n;                                           // keys scanned per step
+    while (st.hi > 0) {
+        if (st.m <= kRank) {
+            __syncthreads();                               // hist and sh are free
+            if (tid == 0) sh[3] = 0;
+            __syncthreads();
+            for (int j = tid; j < cnt; j += kTkThreads) {
+                const uint32_t u = in_short ? shortl[j] : keys[P(j)];
+                if ((u & st.pmask) == st.prefix) hist[atomicAdd(&sh[3], 1)] = u;
+            }
+            __syncthreads();
+            rank_list(hist, st.m, st.need, sh);
+            __syncthreads();
+            st.prefix = (uint32_t)sh[4];
+            st.need = sh[5];
+            st.hi = 0;
+            return;
+        }
+        if (!in_short && st.m <= kShort) {
+            __syncthreads();                               // every thread has read sh
+            if (tid == 0) sh[3] = 0;
+            __syncthreads();
+            for (int j = tid; j < n; j += kTkThreads) {
+                const uint32_t u = keys[P(j)];
+                if ((u & st.pmask) == st.prefix) shortl[atomicAdd(&sh[3], 1)] = u;
+            }
+            in_short = true;
+            cnt = st.m;
+        }
+        const int lo = max(st.hi - 8, 0);
+        const uint32_t dmask = (1u << (st.hi - lo)) - 1u;
+        __syncthreads();                                   // previous step done with hist/sh
+        for (int i = tid; i < 256 * kHistCopies; i += kTkThreads) hist[i] = 0;
+        __syncthreads();
+        // kHistCopies copies of every bin, picked by lane, so lanes counting the
+        // same digit hit different banks instead of serialising on one word
+        const int copy = tid & (kHistCopies - 1);
+        for (int j = tid; j < cnt; j += kTkThreads) {
+            const uint32_t u = in_short ? shortl[j] : keys[P(j)];
+            if ((u & st.pmask) == st.prefix)
+                atomicAdd(&hist[((u >> lo) & dmask) * kHistCopies + copy], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) digit_search(hist, st.need, sh);
+        __syncthreads();
+        st.prefix |= (uint32_t)sh[0] << lo;
+        st.pmask |= dmask << lo;
+        st.need = sh[1];
+        st.m = sh[2];
+        st.hi = lo;
+    }
+}
+
+// n > kRegCap: keys in the global scratch area (plain layout).
+template <bool IN_LDS>
+__device__ void topk_global(const float* __restrict__ rb, const int32_t* __restrict__ cand, int n,
+                            int k, uint32_t* keys, int32_t* __restrict__ out, unsigned* hist,
+                            uint32_t* shortl, int* scratch, int* sh) {
+    auto P = [](int j) { return IN_LDS ? j + (j >> 5) : j; };
+    const int tid = threadIdx.x;
+    // Gather the keys, 8 independent loads in flight per thread.  The AND and OR
+    // of all keys give the bits every candidate shares.
     uint32_t kand = ~0u, kor = 0u;
     for (int j0 = tid; j0 < n; j0 += 8 * kTkThreads) {
         int c[8];
@@ -95,74 +428,13 @@ __device__ void topk_body(const float* __restrict__ rb, const int32_t* __restric
         kand &= (uint32_t)scratch[i];
         kor |= (uint32_t)scratch[kTkWaves + i];
     }
-
-    // Radix select over the bits where candidates differ, most significant
-    // first, 8 bits per pass: histogram the digit among keys that match the
-    // prefix fixed so far, then keep the digit holding the need-th largest key.
     const uint32_t diff = kand ^ kor;
     const int top = diff ? 31 - __clz(diff) : -1;          // highest differing bit
-    uint32_t pmask = top >= 31 ? 0u : (~0u << (top + 1));
-    uint32_t prefix = kand & pmask;
-    int need = k;
-    for (int hi = top + 1; hi > 0;) {
-        const int lo = max(hi - 8, 0);
-        const uint32_t dmask = (1u << (hi - lo)) - 1u;
-        __syncthreads();                                   // previous pass done with hist/sh
-        for (int i = tid; i < 256 * kHistCopies; i += kTkThreads) hist[i] = 0;
-        __syncthreads();
-        // kHistCopies copies of every bin, picked by lane, so lanes counting the
-        // same digit hit different banks instead of serialising on one word
-        const int copy = tid & (kHistCopies - 1);
-        for (int j = tid; j < n; j += kTkThreads) {
-            const uint32_t u = keys[P(j)];
-            if ((u & pmask) == prefix) atomicAdd(&hist[((u >> lo) & dmask) * kHistCopies + copy], 1u);
-        }
-        __syncthreads();
-        if (tid < 64) {
-            // lane l owns digits 4l..4l+3; find the digit d with
-            // (#keys with digit > d) < need <= (#keys with digit >= d).
-            int cnt[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4* hq = reinterpret_cast<const u32x4*>(&hist[(4 * tid + q) * kHistCopies]);
-                int t = 0;
-#pragma unroll
-                for (int i = 0; i < kHistCopies / 4; ++i) {
-                    const u32x4 v = hq[i];
-                    t += (int)(v[0] + v[1] + v[2] + v[3]);
-                }
-                cnt[q] = t;
-            }
-            const int c0 = cnt[0], c1 = cnt[1], c2 = cnt[2], c3 = cnt[3];
-            const int tot = c0 + c1 + c2 + c3;
-            int suf = tot;  // inclusive suffix sum over lanes >= tid
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_down(suf, off);
-                if (tid + off < 64) suf += y;
-            }
-            const int above = suf - tot;  // keys with a digit in higher lanes
-            if (above < need && need <= suf) {
-                int acc = above, d = 4 * tid + 3;
-                const int cs[4] = {c0, c1, c2, c3};
-                for (int q = 3; q >= 0; --q) {
-                    if (acc + cs[q] >= need) {
-                        d = 4 * tid + q;
-                        break;
-                    }
-                    acc += cs[q];
-                }
-                sh[0] = d;
-                sh[1] = need - acc;
-            }
-        }
-        __syncthreads();
-        prefix |= (uint32_t)sh[0] << lo;
-        pmask |= dmask << lo;
-        need = sh[1];
-        hi = lo;
-    }
-    const uint32_t U = prefix;
+    const uint32_t pmask = top >= 31 ? 0u : (~0u << (top + 1));
+    RadixState st{kand & pmask, pmask, top + 1, n, k};
+    radix_refine<IN_LDS>(keys, n, st, hist, shortl, sh);
+    const uint32_t U = st.prefix;
+    const int need = st.need;
 
     // Ordered compaction: thread t walks candidates [t*per, (t+1)*per).  The
     // first 16 candidate indices of the run are fetched now, so their latency
@@ -210,10 +482,10 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
     const int32_t* __restrict__ seq_len, int64_t max_len, const int32_t* __restrict__ cand_idx,
     const int32_t* __restrict__ cand_count, int k, int32_t* __restrict__ topk_idx,
     int32_t* __restrict__ topk_count, uint32_t* __restrict__ gkeys) {
-    __shared__ uint32_t skeys[kCapPadded];
-    __shared__ __attribute__((aligned(16))) unsigned hist[256 * kHistCopies];
+    __shared__ __attribute__((aligned(16))) unsigned hist[kHistWords];
+    __shared__ __attribute__((aligned(16))) uint32_t shortl[kShort];
     __shared__ int scratch[2 * kTkWaves];
-    __shared__ int sh[2];
+    __shared__ int sh[8];
     const int b = blockIdx.x;
     const int64_t S = min((int64_t)seq_len[b], max_len);
     const int n = (int)max((int64_t)0, min((int64_t)cand_count[b], S));
@@ -225,10 +497,11 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
         if (threadIdx.x == 0) topk_count[b] = n;
         return;
     }
-    if (n <= kCap)
-        topk_body<true>(r + eo, cand, n, k, skeys, out, hist, scratch, sh);
+    if (n <= kRegCap)
+        topk_regs(r + eo, cand, n, k, out, hist, shortl, scratch, sh);
     else
-        topk_body<false>(r + eo, cand, n, k, gkeys + (int64_t)b * max_len, out, hist, scratch, sh);
+        topk_global<false>(r + eo, cand, n, k, gkeys + (int64_t)b * max_len, out, hist, shortl,
+                           scratch, sh);
     if (threadIdx.x == 0) topk_count[b] = k;
 }
 
@@ -237,7 +510,7 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
 using namespace lsa;
 
 size_t lsa_topk_workspace(int B, int64_t max_len) {
-    return max_len > kCap ? sizeof(uint32_t) * (size_t)B * (size_t)max_len : 0;
+    return max_len > kRegCap ? sizeof(uint32_t) * (size_t)B * (size_t)max_len : 0;
 }
 
 extern "C" int lsa_topk(const float* rank_key, const int64_t* entry_start, const int32_t* seq_len,
