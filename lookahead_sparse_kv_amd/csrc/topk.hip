@@ -27,7 +27,7 @@ namespace lsa {
 
 constexpr int kTkThreads = 1024;
 constexpr int kTkWaves = kTkThreads / kWave;
-constexpr int kRunChunks = 32;                   // 64-candidate chunks per wave held in registers
+constexpr int kRunChunks = 32;                   // most 64-candidate chunks per wave in registers
 constexpr int kRegCap = kTkWaves * kRunChunks * kWave;  // 32768 candidates
 constexpr int kHistCopies = 16;                  // lane-spread copies of each 8-bit radix bin
 constexpr int kShort = 2048;                     // longest digit list copied to the short list
@@ -154,6 +154,10 @@ __device__ __forceinline__ void rank_list(const uint32_t* list, int m, int need,
 
 // n <= kRegCap: candidates in registers.  Wave w holds chunks [w*cpw, (w+1)*cpw)
 // of 64 consecutive candidates; lane l of chunk u is candidate (w*cpw + u)*64 + l.
+// RC >= cpw is the register window: every per-chunk loop is unrolled RC times
+// and the code runs once per workgroup, so the caller picks the smallest RC
+// that fits (instruction fetch of unused chunk bodies costs real time).
+template <int RC>
 __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restrict__ cand, int n,
                           int k, int32_t* __restrict__ out, unsigned* hist, uint32_t* shortl,
                           int* scratch, int* sh) {
@@ -162,27 +166,27 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
     const int wave = tid >> 6;
     const int cpw = (n + kTkWaves * kWave - 1) / (kTkWaves * kWave);
     const int wb = wave * cpw * kWave;
-    uint32_t kr[kRunChunks];
-    int cr[kRunChunks];
+    uint32_t kr[RC];
+    int cr[RC];
     // gather: candidate indices, then their keys (every load of the run in flight);
     // the histogram is cleared meanwhile
 #pragma unroll
-    for (int u = 0; u < kRunChunks; ++u) {
+    for (int u = 0; u < RC; ++u) {
         cr[u] = 0;
         if (u < cpw) cr[u] = cand[min(wb + kWave * u + lane, n - 1)];
     }
     for (int i = tid; i < kHistWords / 4; i += kTkThreads)
         reinterpret_cast<u32x4*>(hist)[i] = u32x4{0u, 0u, 0u, 0u};
-    float v[kRunChunks];
+    float v[RC];
 #pragma unroll
-    for (int u = 0; u < kRunChunks; ++u) {
+    for (int u = 0; u < RC; ++u) {
         v[u] = 0.0f;
         if (u < cpw) v[u] = rb[cr[u]];
     }
     __syncthreads();                                       // histogram cleared
     const int copy = lane & (kCopies0 - 1);
 #pragma unroll
-    for (int u = 0; u < kRunChunks; ++u) {
+    for (int u = 0; u < RC; ++u) {
         kr[u] = 0u;
         if (u < cpw) {
             const bool in = wb + kWave * u + lane < n;
@@ -237,7 +241,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
                 }
             } else {
 #pragma unroll
-                for (int u = 0; u < kRunChunks; ++u)
+                for (int u = 0; u < RC; ++u)
                     if (valid(u) && (kr[u] & pmask) == prefix) hist[atomicAdd(&sh[3], 1)] = kr[u];
             }
             __syncthreads();
@@ -253,7 +257,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
             if (tid == 0) sh[3] = 0;
             __syncthreads();
 #pragma unroll
-            for (int u = 0; u < kRunChunks; ++u)
+            for (int u = 0; u < RC; ++u)
                 if (valid(u) && (kr[u] & pmask) == prefix) shortl[atomicAdd(&sh[3], 1)] = kr[u];
             __syncthreads();
             if (tid == 0) sh[6] = sh[3];                   // list length
@@ -273,7 +277,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < kRunChunks; ++u)
+            for (int u = 0; u < RC; ++u)
                 if (valid(u) && (kr[u] & pmask) == prefix)
                     atomicAdd(&hist[((kr[u] >> lo) & dmask) * kHistCopies + hcopy], 1u);
         }
@@ -292,7 +296,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
     // then every chunk writes its selected candidates contiguously.
     int gt_w = 0, eq_w = 0;
 #pragma unroll
-    for (int u = 0; u < kRunChunks; ++u) {
+    for (int u = 0; u < RC; ++u) {
         if (u < cpw) {
             const bool in = valid(u);
             gt_w += __popcll(__ballot(in && kr[u] > U));
@@ -312,7 +316,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
         eqs += e2;
     }
 #pragma unroll
-    for (int u = 0; u < kRunChunks; ++u) {
+    for (int u = 0; u < RC; ++u) {
         if (u < cpw) {                                     // uniform
             const bool in = valid(u);
             const bool g = in && kr[u] > U;
@@ -497,8 +501,15 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
         if (threadIdx.x == 0) topk_count[b] = n;
         return;
     }
-    if (n <= kRegCap)
-        topk_regs(r + eo, cand, n, k, out, hist, shortl, scratch, sh);
+    const int cpw = (n + kTkWaves * kWave - 1) / (kTkWaves * kWave);   // chunks per wave
+#define LSA_TK_REGS(rc)                                                        \
+    else if (cpw <= rc) topk_regs<rc>(r + eo, cand, n, k, out, hist, shortl, scratch, sh);
+    if (false) {
+    }
+    // steps of 8 chunks: finer steps make workgroups of one launch run different
+    // bodies, which then share fewer instruction-cache lines (measured slower)
+    LSA_TK_REGS(8) LSA_TK_REGS(16) LSA_TK_REGS(24) LSA_TK_REGS(kRunChunks)
+#undef LSA_TK_REGS
     else
         topk_global<false>(r + eo, cand, n, k, gkeys + (int64_t)b * max_len, out, hist, shortl,
                            scratch, sh);
