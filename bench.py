@@ -171,22 +171,25 @@ def main():
 
         # Steps and per-kernel runs are replayed from HIP graphs (no host work in
         # the timed region); replicas rotate so reads come from HBM, not the cache.
+        # The W warm-up steps form one graph and the K timed steps another, as a
+        # decode loop captures its steps: every step runs all four calls on its own
+        # replica, and no per-step graph launch sits between steps.
         nrot = max(rk, rl)
-        for i in range(max(args.warmup, 1)):
-            p.step(i)
+        p.step(0)
         torch.cuda.synchronize()
-        step_graphs = [capture(torch, stream, [lambda i=i: p.step(i)]) for i in range(nrot)]
-        for i in range(args.warmup):
-            step_graphs[i % nrot].replay()
+        if args.warmup:
+            capture(torch, stream, [lambda i=i: p.step(i) for i in range(args.warmup)]).replay()
+        timed = capture(torch, stream,
+                        [lambda i=i: p.step((args.warmup + i) % nrot) for i in range(args.steps)])
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(args.steps):
-            step_graphs[i % nrot].replay()
+        timed.replay()
         e1.record(stream)
         torch.cuda.synchronize()
         step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
+        del timed
 
         # per-kernel launch durations: graphs of R back-to-back launches of one call
         def reps_for(est_s):
@@ -200,7 +203,6 @@ def main():
         r = reps_for(step_s / 4)
         t_attend = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.attend(i) for i in range(r)]), r)
-        del step_graphs
 
     torch.cuda.synchronize()
     counts = p.cand_count.cpu().numpy()
