@@ -133,15 +133,15 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     // and barriers below instead of draining all copies before each LDS read.
     constexpr int OFF_PBUF = NB * kChunk * Dl * 2;          // ring: NB slots of kChunk rows
     constexpr int OFF_SMAX = OFF_PBUF + kMQ * PROW * 2;     // P (bf16)
-    constexpr int OFF_SSUM = OFF_SMAX + 2 * kMQ * 4;        // chunk maxima of the two row tiles
-    constexpr int OFF_ABUF = OFF_SSUM + 2 * kMQ * 4;        // and their sums of P
+    constexpr int OFF_FLAG = OFF_SMAX + 2 * kMQ * 4;        // chunk maxima of the two row tiles
+    constexpr int OFF_ABUF = OFF_FLAG + 16;                 // per-wave "running max moves" flags
     constexpr int OFF_ML = OFF_ABUF + kMQ * 4;              // rescale factors of O
     constexpr int LDS_BYTES = OFF_ML + 2 * kMQ * 4;         // final (m, l)
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     bf16* const ring0 = reinterpret_cast<bf16*>(lds);
     bf16* const pbuf = reinterpret_cast<bf16*>(lds + OFF_PBUF);
     float (*const smax)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_SMAX);
-    float (*const ssum)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_SSUM);
+    int* const flags = reinterpret_cast<int*>(lds + OFF_FLAG);
     float* const abuf = reinterpret_cast<float*>(lds + OFF_ABUF);
     float (*const mlbuf)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_ML);
 
@@ -204,12 +204,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) o[h2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // wave 0 also accumulates P . 1: the row sums l of P, rescaled with O
+    f32x4 ol[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
     // running max (base 2) and sum of query rows 16ht + 4g + v (sums kept by rt == 0)
-    float m_ref[4], l_run[4];
+    float m_ref[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         m_ref[v] = -INFINITY;
-        l_run[v] = 0.0f;
     }
 
     // Chunk c -> ring slot c % NB.  Instruction i of copy wave p moves chunk rows
@@ -274,53 +275,58 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         // this lane holds query rows q0 + v (v = 0..3) against chunk row 16rt + n16
         const int q0 = 16 * ht + 4 * g;
         const bool valid = r0 + 16 * rt + n16 < re;
-        f32x4 x, cm;
+        f32x4 x;
 #pragma unroll
         for (int v = 0; v < 4; ++v) x[v] = valid ? sacc[v] * scale_log2 : -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) cm[v] = group_max<16>(x[v]);
-        if (n16 == 0) *reinterpret_cast<f32x4*>(&smax[rt][q0]) = cm;
-        lds_barrier();
-        const f32x4 ma = *reinterpret_cast<const f32x4*>(&smax[0][q0]);
-        const f32x4 mb = *reinterpret_cast<const f32x4*>(&smax[1][q0]);
-        // Lazy rescale, branch-free: the running max moves only when the chunk max
-        // exceeds it by more than kRescaleSlack (always on the first chunk, as
-        // -inf + slack = -inf); then alpha = 2^(m_old - m_new), 0 on the first
-        // chunk.  x - m_ref <= kRescaleSlack afterwards, so p <= 2^kRescaleSlack.
-        f32x4 alpha, ps;
+        // Fast path: P against the running max, which stands unless some logit of
+        // the chunk exceeds it by more than kRescaleSlack (lazy rescale; always on
+        // the first chunk, as -inf + slack = -inf).  p <= 2^kRescaleSlack.
+        bool over = false;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const float cmax = fmaxf(ma[v], mb[v]);
-            const bool grow = cmax > m_ref[v] + kRescaleSlack;
-            alpha[v] = grow ? __builtin_amdgcn_exp2f(m_ref[v] - cmax) : 1.0f;
-            m_ref[v] = grow ? cmax : m_ref[v];
+            over = over || x[v] > m_ref[v] + kRescaleSlack;
             const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
-            const bf16 pb = (bf16)p;
-            pbuf[(q0 + v) * PROW + 16 * rt + n16] = pb;
-            ps[v] = (float)pb;
+            pbuf[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
         }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) ps[v] = group_sum<16>(ps[v]);
-        if (n16 == 0) {
-            *reinterpret_cast<f32x4*>(&ssum[rt][q0]) = ps;
-            if (rt == 0) *reinterpret_cast<f32x4*>(&abuf[q0]) = alpha;
-        }
+        const bool wave_over = __ballot(over) != 0;
+        if (lane == 0) flags[wave] = wave_over ? 1 : 0;
         lds_barrier();
-        if (rt == 0) {
-            const f32x4 sa = *reinterpret_cast<const f32x4*>(&ssum[0][q0]);
-            const f32x4 sb = *reinterpret_cast<const f32x4*>(&ssum[1][q0]);
+        const bool slow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;   // uniform
+        if (slow) {
+            // Slow path: the chunk maxima of the two row tiles meet, the running
+            // max moves where it grew by more than the slack (alpha = 2^(m_old -
+            // m_new), 0 on the first chunk), and P is recomputed against it.
+            f32x4 cm;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) l_run[v] = alpha[v] * l_run[v] + (sa[v] + sb[v]);
-        }
-        // rescale O rows whose running max moved
+            for (int v = 0; v < 4; ++v) cm[v] = group_max<16>(x[v]);
+            if (n16 == 0) *reinterpret_cast<f32x4*>(&smax[rt][q0]) = cm;
+            lds_barrier();
+            const f32x4 ma = *reinterpret_cast<const f32x4*>(&smax[0][q0]);
+            const f32x4 mb = *reinterpret_cast<const f32x4*>(&smax[1][q0]);
+            f32x4 alpha;
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * h2 + 4 * g]);
-            if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {
+            for (int v = 0; v < 4; ++v) {
+                const float cmax = fmaxf(ma[v], mb[v]);
+                const bool grow = cmax > m_ref[v] + kRescaleSlack;
+                alpha[v] = grow ? __builtin_amdgcn_exp2f(m_ref[v] - cmax) : 1.0f;
+                m_ref[v] = grow ? cmax : m_ref[v];
+                const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
+                pbuf[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
+            }
+            if (rt == 0 && n16 == 0) *reinterpret_cast<f32x4*>(&abuf[q0]) = alpha;
+            lds_barrier();
+            // rescale O (and wave 0's row sums) rows whose running max moved
 #pragma unroll
-                for (int nt = 0; nt < NDT; ++nt)
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * h2 + 4 * g]);
+                if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) o[h2][nt][v] *= al[v];
+                    for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) o[h2][nt][v] *= al[v];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) ol[h2][v] *= al[v];
+                }
             }
         }
         // P C over this wave's dims.  A: query row 16h2 + n16, chunk rows 8g .. 8g+7.
@@ -331,6 +337,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
             pa[h2] = *reinterpret_cast<const bf16x8*>(&pbuf[(16 * h2 + n16) * PROW + 8 * g]);
+        if (wave == 0) {
+            bf16x8 ones;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) ol[h2] = mfma16(pa[h2], ones, ol[h2]);
+        }
         const int trow0 = 8 * g + (n16 >> 2);
         const int trow1 = trow0 + 4;
         const int sw0 = slot_swz(trow0), sw1 = slot_swz(trow1);
@@ -364,9 +377,11 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     };
 
     // Pipeline: the copy waves keep NB-1 chunks staged ahead of the compute
-    // waves.  Three barriers per chunk, taken by all eight waves: B0 (chunk c is
-    // in LDS; every read of chunk c-1 has retired, so its slot is refilled right
-    // after) and the two inside process(c).
+    // waves.  Barriers per chunk, taken by all eight waves: B0 (chunk c is in
+    // LDS; every read of chunk c-1 has retired, so its slot is refilled right
+    // after), B1 (P and the flags are published) and, when some flag is set, the
+    // two of the slow path inside process(c).  Every wave reads the flags after
+    // B1, so all take the same path; they are rewritten only after the next B0.
     if (copier) {
 #pragma unroll
         for (int c = 0; c < NB - 1; ++c)
@@ -377,10 +392,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             else if (after == 1) wait_vmcnt<IPW>();
             else wait_vmcnt<0>();
             static_assert(NB <= 4, "the waits above cover two later chunks");
-            lds_barrier();
+            lds_barrier();                                      // chunk c staged
             if (c + NB - 1 < nchunks) issue_chunk(c + NB - 1);
-            lds_barrier();
-            lds_barrier();
+            lds_barrier();                                      // P published, flags set
+            if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+                lds_barrier();                                  // slow path: maxima met
+                lds_barrier();                                  // slow path: P republished
+            }
         }
         // the two barriers of the output stage below
         lds_barrier();
@@ -396,10 +414,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     // (ring slot 0, free now) so the stores to HBM are 16 bytes per lane
     if (rt == 0 && n16 == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            mlbuf[0][16 * ht + 4 * g + v] = m_ref[v];
-            mlbuf[1][16 * ht + 4 * g + v] = l_run[v];
-        }
+        for (int v = 0; v < 4; ++v) mlbuf[0][16 * ht + 4 * g + v] = m_ref[v];
+    }
+    if (wave == 0 && n16 == 0) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mlbuf[1][16 * h2 + 4 * g + v] = ol[h2][v];
     }
     lds_barrier();
     bf16* ost = ring0 + wave * (kMQ * DPW);
