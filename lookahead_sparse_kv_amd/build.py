@@ -30,9 +30,15 @@ COMMON = [
 ]
 
 
+# Per-source additions.  attend.hip: the first 16 dwords of kernel arguments are
+# preloaded into scalar registers at wave launch (the code object keeps a
+# fallback entry that loads them for firmware without preloading).
+EXTRA = {"attend.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + EXTRA.get(src, []) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -53,9 +53,8 @@ __device__ __forceinline__ const E* att_row(int j, int nt, int n, const E* laten
 __device__ __forceinline__ int xcd_item(int n_items) {
     const int per_xcd = (n_items + 7) / 8;
     const int slot = blockIdx.x >> 3;
-    if (slot >= per_xcd) return -1;
     const int item = (blockIdx.x & 7) * per_xcd + slot;
-    return item < n_items ? item : -1;
+    return (slot < per_xcd && item < n_items) ? item : -1;
 }
 
 // 16-byte slot swizzle of a staged latent row (a multiple of 16 slots, so every
@@ -107,14 +106,17 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
 }
 
+// Parameter order: what the first loads need comes first (14 dwords: the work
+// item, the Q and index addresses, the count pointers), so a build that
+// preloads kernel arguments into scalar registers issues them at launch.
 template <int Dl, int NB>
 __global__ __launch_bounds__(512, 1) void k_attend_mfma(
-    const bf16* __restrict__ qa, int M, const bf16* __restrict__ latent,
-    const int64_t* __restrict__ latent_row_start, const int32_t* __restrict__ topk_idx,
-    const int32_t* __restrict__ topk_count, int k, const bf16* __restrict__ hca,
-    const int64_t* __restrict__ hca_row_start, const int32_t* __restrict__ hca_count,
-    int64_t max_hca, float scale_log2, int QG, int nsplit, int rows_per_split, int n_items,
-    bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
+    int n_items, int QG, int nsplit, int rows_per_split, int M, int k,
+    const int32_t* __restrict__ topk_idx, const bf16* __restrict__ qa,
+    const int32_t* __restrict__ topk_count, const int32_t* __restrict__ hca_count,
+    const int64_t* __restrict__ latent_row_start, const int64_t* __restrict__ hca_row_start,
+    int64_t max_hca, const bf16* __restrict__ latent, const bf16* __restrict__ hca,
+    float scale_log2, bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
     float* __restrict__ part_lse) {
     constexpr int NW = 4;                       // compute waves (waves 0..3)
     constexpr int NP = 4;                       // copy waves (waves 4..7)
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     // the direct-to-LDS copies and the LDS reads to the explicit counted waits
     // and barriers below instead of draining all copies before each LDS read.
     constexpr int OFF_PBUF = NB * kChunk * Dl * 2;          // ring: NB slots of kChunk rows
-    constexpr int OFF_SMAX = OFF_PBUF + kMQ * PROW * 2;     // P (bf16)
+    constexpr int OFF_SMAX = OFF_PBUF + 2 * kMQ * PROW * 2; // P (bf16), two buffers
     constexpr int OFF_FLAG = OFF_SMAX + 2 * kMQ * 4;        // chunk maxima of the two row tiles
-    constexpr int OFF_ABUF = OFF_FLAG + 16;                 // per-wave "running max moves" flags
+    constexpr int OFF_ABUF = OFF_FLAG + 32;                 // per-wave "running max moves" flags, two sets
     constexpr int OFF_ML = OFF_ABUF + kMQ * 4;              // rescale factors of O
     constexpr int LDS_BYTES = OFF_ML + 2 * kMQ * 4;         // final (m, l)
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
@@ -145,11 +147,18 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     float* const abuf = reinterpret_cast<float*>(lds + OFF_ABUF);
     float (*const mlbuf)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_ML);
 
-    const int item = xcd_item(n_items);
-    if (item < 0) return;
-    const int qg = item % QG;
-    const int split = (item / QG) % nsplit;
-    const int b = item / (QG * nsplit);
+    // Work item and per-sequence values.  Every load here is unconditional (a
+    // stand-in pointer replaces a missing HCA pool), so they issue together in
+    // one round trip after the kernel arguments instead of one after another.
+    // A workgroup past the last item (the grid is a multiple of 8) runs item 0
+    // with no rows and stores nothing.
+    const int item_raw = xcd_item(n_items);
+    const bool active = item_raw >= 0;
+    const int item = active ? item_raw : 0;
+    const int tq = item / QG;
+    const int qg = item - tq * QG;
+    const int b = tq / nsplit;
+    const int split = tq - b * nsplit;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -160,25 +169,23 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     const int rt = (wave >> 1) & 1;             // Q K^T: chunk rows 16rt .. 16rt+15
     const int ht = wave & 1;                    //        query rows 16ht .. 16ht+15
 
-    const int ntop = min(topk_count[b], k);
-    const int nh = hca ? (int)min((int64_t)hca_count[b], max_hca) : 0;
-    const int n = ntop + nh;
     const int rs = split * rows_per_split;
-    const int re = min(n, rs + rows_per_split);
-    const int64_t lrs = latent_row_start[b];
-    const int64_t hrs = hca ? hca_row_start[b] : 0;
     const int32_t* idx = topk_idx + (int64_t)b * k;
-    const int nchunks = re > rs ? (re - rs + kChunk - 1) / kChunk : 0;
     const int64_t qrow0 = (int64_t)b * M + (int64_t)qg * kMQ;   // first query row of the group
     const int mq = min(kMQ, M - qg * kMQ);                        // valid query rows
 
     // Q fragments (A operand): query row 16ht + n16, dims 32kk + 8g .. +7
     bf16x8 qf[KDT];
     if (!copier) {
+        // rows past the group's end read its first row and are zeroed after
         const bool ok = 16 * ht + n16 < mq;
         const bf16* qp = qa + (qrow0 + (ok ? 16 * ht + n16 : 0)) * Dl + 8 * g;
 #pragma unroll
-        for (int kk = 0; kk < KDT; ++kk) qf[kk] = ok ? load8(qp + 32 * kk) : zero8();
+        for (int kk = 0; kk < KDT; ++kk) qf[kk] = load8(qp + 32 * kk);
+        if (!ok) {
+#pragma unroll
+            for (int kk = 0; kk < KDT; ++kk) qf[kk] = zero8();
+        }
     }
     // Copy wave p stages rows 8p .. 8p+7 of every chunk.  Lane c holds the
     // chosen-entry indices of those rows of chunk c (a split has at most 64
@@ -194,11 +201,41 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             ridx[j8] = idx[min(rs + kChunk * lane + 8 * (wave - NW) + j8, k - 1)];
         first_idx = idx[min(rs, k - 1)];
     }
+    // The per-sequence counts and row starts load while the vector loads above
+    // are in flight.
+    const int topk_cnt = topk_count[b];
+    const int hca_cnt = hca_count[b];
+    const int64_t lrs = latent_row_start[b];
+    const int64_t hrs = hca_row_start[b];
+    const int ntop = min(topk_cnt, k);
+    const int nh = (int)min((int64_t)hca_cnt, max_hca);   // max_hca = 0 without a pool
+    const int n = ntop + nh;
+    const int re = min(n, rs + rows_per_split);
+    const int nchunks = (active && re > rs) ? (re - rs + kChunk - 1) / kChunk : 0;
     // Q (compute waves) and the indices (copy waves) are complete before the
     // loop.  Only the copy waves issue copies, so their counted waits below are
     // exact, and the compute waves never have a copy outstanding when they read
     // LDS.
     wait_vmcnt<0>();
+    // Copy waves: the 64-bit address of every row they stage, computed once
+    // (lane c holds rows 8p .. 8p+7 of chunk c, p = wave - NW), so a copy costs
+    // two lane reads and no branches.  Rows past the split end re-read the
+    // split's first row (finite data, probability zero).
+    uint32_t raddr_lo[8], raddr_hi[8];
+    if (copier) {
+        const uint64_t lat = (uint64_t)latent, hc = (uint64_t)hca;
+#pragma unroll
+        for (int j8 = 0; j8 < 8; ++j8) {
+            const int j0 = rs + kChunk * lane + 8 * (wave - NW) + j8;
+            const bool past = j0 >= re;
+            const int j = past ? rs : j0;
+            const int e = past ? first_idx : ridx[j8];
+            const uint64_t a = j < ntop ? lat + (uint64_t)(lrs + e) * (uint64_t)(Dl * 2)
+                                        : hc + (uint64_t)(hrs + (j - ntop)) * (uint64_t)(Dl * 2);
+            raddr_lo[j8] = (uint32_t)a;
+            raddr_hi[j8] = (uint32_t)(a >> 32);
+        }
+    }
     f32x4 o[2][NDT];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2)
@@ -218,23 +255,21 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     // slot (L % SL) ^ swz(r).  Rows past the split end re-read its first row
     // (finite data, probability zero).
     auto issue_chunk = [&](int c) {
-        const int r0 = rs + c * kChunk;
         bf16* slot = ring0 + (c % NB) * (kChunk * Dl);
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int sub = lane / SL;                     // row of this lane in the instruction
             const int rbase = 8 * (wave - NW) + RPI * i;
             const int rl = rbase + sub;
-            int e = __builtin_amdgcn_readlane(ridx[RPI * i], c);
+            uint32_t lo = __builtin_amdgcn_readlane(raddr_lo[RPI * i], c);
+            uint32_t hi = __builtin_amdgcn_readlane(raddr_hi[RPI * i], c);
 #pragma unroll
             for (int s2 = 1; s2 < RPI; ++s2)
-                if (sub == s2) e = __builtin_amdgcn_readlane(ridx[RPI * i + s2], c);
-            int j = r0 + rl;
-            if (j >= re) {
-                j = rs;
-                e = first_idx;
-            }
-            const bf16* row = j < ntop ? latent + (lrs + e) * Dl : hca + (hrs + (j - ntop)) * Dl;
+                if (sub == s2) {
+                    lo = __builtin_amdgcn_readlane(raddr_lo[RPI * i + s2], c);
+                    hi = __builtin_amdgcn_readlane(raddr_hi[RPI * i + s2], c);
+                }
+            const bf16* row = reinterpret_cast<const bf16*>(((uint64_t)hi << 32) | lo);
             __builtin_amdgcn_global_load_lds(
                 (const void*)(row + 8 * ((lane % SL) ^ slot_swz(rl))),
                 (__attribute__((address_space(3))) void*)(slot + rbase * Dl), 16, 0, 0);
@@ -242,26 +277,34 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     };
 
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    auto process = [&](int c) {
+    // Q K^T of chunk c, then P against the running max into pbuf[c & 1] and this
+    // wave's "running max must move" flag into flags[c & 1].  Returns the
+    // base-2 logits (kept for the slow path).
+    auto qk_p = [&](int c) -> f32x4 {
         const int r0 = rs + c * kChunk;
         const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
         // S tile: D[4g+v][n16] = query row 16ht + 4g + v against chunk row 16rt + n16
         f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
         {
             const int r = 16 * rt + n16;
-            const bf16* rp = sl + r * Dl;
             const int sw = slot_swz(r);
+            // logical slot 4kk + g sits at physical ((4(kk & 3) + g) ^ sw) + 16(kk >> 2):
+            // the swizzle only touches the low four slot bits, so four base
+            // addresses and immediate offsets cover every step
+            const bf16* kp[4];
+#pragma unroll
+            for (int b4 = 0; b4 < 4; ++b4) kp[b4] = sl + r * Dl + 8 * ((4 * b4 + g) ^ sw);
             // K operands through an 8-deep register window: 8 reads stay in flight
             constexpr int KW = KDT < 8 ? KDT : 8;
             bf16x8 kb[KW];
 #pragma unroll
             for (int kk = 0; kk < KW; ++kk)
-                kb[kk] = *reinterpret_cast<const bf16x8*>(rp + 8 * ((4 * kk + g) ^ sw));
+                kb[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
 #pragma unroll
             for (int kk = 0; kk < KDT; ++kk) {
                 sacc = mfma16(qf[kk], kb[kk % KW], sacc);
                 if (kk + KW < KDT)
-                    kb[kk % KW] = *reinterpret_cast<const bf16x8*>(rp + 8 * ((4 * (kk + KW) + g) ^ sw));
+                    kb[kk % KW] = *reinterpret_cast<const bf16x8*>(kp[(kk + KW) & 3] + 128 * ((kk + KW) >> 2));
             }
             // schedule: the first KW reads, then one product per refill read
             __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);
@@ -281,54 +324,24 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         // Fast path: P against the running max, which stands unless some logit of
         // the chunk exceeds it by more than kRescaleSlack (lazy rescale; always on
         // the first chunk, as -inf + slack = -inf).  p <= 2^kRescaleSlack.
+        bf16* pb = pbuf + (c & 1) * (kMQ * PROW);
         bool over = false;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             over = over || x[v] > m_ref[v] + kRescaleSlack;
             const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
-            pbuf[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
+            pb[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
         }
         const bool wave_over = __ballot(over) != 0;
-        if (lane == 0) flags[wave] = wave_over ? 1 : 0;
-        lds_barrier();
-        const bool slow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;   // uniform
-        if (slow) {
-            // Slow path: the chunk maxima of the two row tiles meet, the running
-            // max moves where it grew by more than the slack (alpha = 2^(m_old -
-            // m_new), 0 on the first chunk), and P is recomputed against it.
-            f32x4 cm;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) cm[v] = group_max<16>(x[v]);
-            if (n16 == 0) *reinterpret_cast<f32x4*>(&smax[rt][q0]) = cm;
-            lds_barrier();
-            const f32x4 ma = *reinterpret_cast<const f32x4*>(&smax[0][q0]);
-            const f32x4 mb = *reinterpret_cast<const f32x4*>(&smax[1][q0]);
-            f32x4 alpha;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float cmax = fmaxf(ma[v], mb[v]);
-                const bool grow = cmax > m_ref[v] + kRescaleSlack;
-                alpha[v] = grow ? __builtin_amdgcn_exp2f(m_ref[v] - cmax) : 1.0f;
-                m_ref[v] = grow ? cmax : m_ref[v];
-                const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
-                pbuf[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
-            }
-            if (rt == 0 && n16 == 0) *reinterpret_cast<f32x4*>(&abuf[q0]) = alpha;
-            lds_barrier();
-            // rescale O (and wave 0's row sums) rows whose running max moved
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * h2 + 4 * g]);
-                if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {
-#pragma unroll
-                    for (int nt = 0; nt < NDT; ++nt)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) o[h2][nt][v] *= al[v];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) ol[h2][v] *= al[v];
-                }
-            }
-        }
+        if (lane == 0) flags[4 * (c & 1) + wave] = wave_over ? 1 : 0;
+        return x;
+    };
+    // After the barrier that publishes chunk c's P and flags: the slow path if
+    // any flag is set, then O[:, dims_w] += P C[:, dims_w].
+    auto pv = [&](int c, f32x4 x) {
+        const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
+        bf16* pb = pbuf + (c & 1) * (kMQ * PROW);
+        const int* fl = flags + 4 * (c & 1);
         // P C over this wave's dims.  A: query row 16h2 + n16, chunk rows 8g .. 8g+7.
         // B from transposing reads: in each 16-lane group, lanes 4j..4j+3 point at
         // chunk row 8g + j (+4 for the upper half), 4 dims each, and lane i receives
@@ -336,14 +349,7 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         bf16x8 pa[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
-            pa[h2] = *reinterpret_cast<const bf16x8*>(&pbuf[(16 * h2 + n16) * PROW + 8 * g]);
-        if (wave == 0) {
-            bf16x8 ones;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) ol[h2] = mfma16(pa[h2], ones, ol[h2]);
-        }
+            pa[h2] = *reinterpret_cast<const bf16x8*>(&pb[(16 * h2 + n16) * PROW + 8 * g]);
         const int trow0 = 8 * g + (n16 >> 2);
         const int trow1 = trow0 + 4;
         const int sw0 = slot_swz(trow0), sw1 = slot_swz(trow1);
@@ -360,6 +366,58 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             hi[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4*)(sl + trow1 * Dl + 8 * (ls ^ sw1) + off));
         }
+        // the flags are read with the operands, so their latency overlaps
+        const bool slow = (fl[0] | fl[1] | fl[2] | fl[3]) != 0;   // uniform
+        if (slow) {
+            // Slow path: the chunk maxima of the two row tiles meet, the running
+            // max moves where it grew by more than the slack (alpha = 2^(m_old -
+            // m_new), 0 on the first chunk), and P is recomputed against it.
+            const int q0 = 16 * ht + 4 * g;
+            const bool valid = rs + c * kChunk + 16 * rt + n16 < re;
+            f32x4 cm;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) cm[v] = group_max<16>(x[v]);
+            if (n16 == 0) *reinterpret_cast<f32x4*>(&smax[rt][q0]) = cm;
+            lds_barrier();
+            const f32x4 ma = *reinterpret_cast<const f32x4*>(&smax[0][q0]);
+            const f32x4 mb = *reinterpret_cast<const f32x4*>(&smax[1][q0]);
+            f32x4 alpha;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const float cmax = fmaxf(ma[v], mb[v]);
+                const bool grow = cmax > m_ref[v] + kRescaleSlack;
+                alpha[v] = grow ? __builtin_amdgcn_exp2f(m_ref[v] - cmax) : 1.0f;
+                m_ref[v] = grow ? cmax : m_ref[v];
+                const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
+                pb[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
+            }
+            if (rt == 0 && n16 == 0) *reinterpret_cast<f32x4*>(&abuf[q0]) = alpha;
+            lds_barrier();
+            // rescale O (and wave 0's row sums) rows whose running max moved
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * h2 + 4 * g]);
+                if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {
+#pragma unroll
+                    for (int nt = 0; nt < NDT; ++nt)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) o[h2][nt][v] *= al[v];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) ol[h2][v] *= al[v];
+                }
+            }
+            // P was rewritten: read the operands again
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+                pa[h2] = *reinterpret_cast<const bf16x8*>(&pb[(16 * h2 + n16) * PROW + 8 * g]);
+        }
+        if (wave == 0) {
+            bf16x8 ones;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) ol[h2] = mfma16(pa[h2], ones, ol[h2]);
+        }
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) {
             bf16x8 cb;
@@ -371,31 +429,38 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) o[h2][nt] = mfma16(pa[h2], cb, o[h2][nt]);
         }
-        // schedule: every LDS read of P and C^T first, then the products
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * NDT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NDT, 0);
     };
 
-    // Pipeline: the copy waves keep NB-1 chunks staged ahead of the compute
-    // waves.  Barriers per chunk, taken by all eight waves: B0 (chunk c is in
-    // LDS; every read of chunk c-1 has retired, so its slot is refilled right
-    // after), B1 (P and the flags are published) and, when some flag is set, the
-    // two of the slow path inside process(c).  Every wave reads the flags after
-    // B1, so all take the same path; they are rewritten only after the next B0.
+    // Pipeline, one barrier per chunk (X_c): before it, every compute wave has
+    // published chunk c's P and flag and finished P C of chunk c-1, and the copy
+    // waves have staged chunk c+1; after it, the copy waves refill chunk c-1's
+    // slot with chunk c+NB-1 while the compute waves run P C of chunk c and
+    // Q K^T of chunk c+1.  P and the flags alternate between two buffers, so the
+    // writes for chunk c+1 never meet a late reader of chunk c.  The slow path
+    // adds two barriers, taken by all eight waves (every wave reads the same
+    // flags after X_c).
     if (copier) {
 #pragma unroll
         for (int c = 0; c < NB - 1; ++c)
             if (c < nchunks) issue_chunk(c);
-        for (int c = 0; c < nchunks; ++c) {
-            const int after = min(nchunks - 1, c + NB - 2) - c;   // chunks issued after c
+        static_assert(NB <= 4, "the waits below cover two later chunks");
+        // X_{-1}: chunk 0 staged
+        {
+            const int after = min(nchunks - 1, NB - 2);   // chunks issued after chunk 0
             if (after >= 2) wait_vmcnt<2 * IPW>();
             else if (after == 1) wait_vmcnt<IPW>();
             else wait_vmcnt<0>();
-            static_assert(NB <= 4, "the waits above cover two later chunks");
-            lds_barrier();                                      // chunk c staged
+        }
+        lds_barrier();
+        for (int c = 0; c < nchunks; ++c) {
+            // chunk c+1 staged before X_c (chunks up to c+NB-2 are issued)
+            const int after = min(nchunks - 1, c + NB - 2) - (c + 1);
+            if (after >= 1) wait_vmcnt<IPW>();
+            else wait_vmcnt<0>();
+            lds_barrier();                                      // X_c
             if (c + NB - 1 < nchunks) issue_chunk(c + NB - 1);
-            lds_barrier();                                      // P published, flags set
-            if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+            const int* fl = flags + 4 * (c & 1);
+            if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
                 lds_barrier();                                  // slow path: maxima met
                 lds_barrier();                                  // slow path: P republished
             }
@@ -405,9 +470,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         lds_barrier();
         return;
     }
+    lds_barrier();                                              // X_{-1}
+    f32x4 xc = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nchunks > 0) xc = qk_p(0);
     for (int c = 0; c < nchunks; ++c) {
-        lds_barrier();
-        process(c);
+        lds_barrier();                                          // X_c
+        pv(c, xc);
+        if (c + 1 < nchunks) xc = qk_p(c + 1);
     }
 
     // publish (m, l); every wave normalises its O columns and stages them in LDS
@@ -445,12 +514,12 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         for (int i = 0; i < kMQ / RPS; ++i) {
             const int ql = RPS * i + lane / LPR;
             const int c8 = 8 * (lane % LPR);
-            if (ql < mq)
+            if (active && ql < mq)
                 *reinterpret_cast<bf16x8*>(dst_base + (int64_t)ql * Dl + DPW * wave + c8) =
                     *reinterpret_cast<const bf16x8*>(ost + ql * DPW + c8);
         }
     }
-    if (tid < mq) {
+    if (active && tid < mq) {
         const float l = mlbuf[1][tid];
         const float v = l > 0.0f ? (mlbuf[0][tid] + log2f(l)) * kLn2 : -INFINITY;
         if (nsplit == 1) {
@@ -670,11 +739,16 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
         const unsigned grid = (unsigned)(8 * ((p.n_items + 7) / 8));
         const float sl2 = scale * kLog2e;
         const int M = T * Hq;
+        // Without an HCA pool the kernel reads valid stand-ins and attends zero
+        // HCA rows (max_hca = 0), so it never branches on the pool.
+        const void* hp = hca ? hca : latent;
+        const int64_t* hrs_p = hca ? hca_row_start : latent_row_start;
+        const int32_t* hcnt_p = hca ? hca_count : topk_count;
 #define LSA_ATT(dl)                                                                            \
     hipLaunchKernelGGL((k_attend_mfma<dl, kAttRing>), dim3(grid), dim3(512), 0, st,             \
-                       (const bf16*)qa, M, (const bf16*)latent, latent_row_start, topk_idx,     \
-                       topk_count, k, (const bf16*)hca, hca_row_start, hca_count, hmax, sl2,    \
-                       p.QG, p.nsplit, p.rows_per_split, p.n_items, (bf16*)out, lse, part_o,    \
+                       p.n_items, p.QG, p.nsplit, p.rows_per_split, M, k, topk_idx,             \
+                       (const bf16*)qa, topk_count, hcnt_p, latent_row_start, hrs_p, hmax,      \
+                       (const bf16*)latent, (const bf16*)hp, sl2, (bf16*)out, lse, part_o,      \
                        part_lse)
         if (Dl == 512) LSA_ATT(512); else if (Dl == 256) LSA_ATT(256); else LSA_ATT(128);
 #undef LSA_ATT
