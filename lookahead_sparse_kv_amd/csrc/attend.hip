@@ -9,32 +9,40 @@
 //
 // Matrix-core kernel (bf16, Dl in {128, 256, 512}).  Every query head of every
 // position of sequence b attends to the same rows, so the (position, head)
-// pairs of b are flattened into M = T * Hq query rows.  A workgroup of four
-// waves takes one (b, group of 32 query rows, row split) and walks its rows in
-// chunks of 32:
-//   1. the chunk's rows are copied from HBM straight into an LDS ring slot
-//      (direct-to-LDS loads, each wave copying a quarter; NB-1 chunks ahead);
-//   2. S = Q K^T: wave w owns the 16 x 16 tile (query rows 16(w&1).., chunk
-//      rows 16(w>>1)..) over the full latent depth, Q held in registers, so
-//      no partial logits cross waves;
-//   3. online softmax in base 2: per-query-row maxima and sums of the two row
-//      tiles meet in LDS, P (bf16) is published there;
-//   4. O[:, dims_w] += P C[:, dims_w]: wave w owns Dl/4 latent dims of all 32
-//      query rows; C^T operands come from transposing LDS reads of the slot.
-// Rows are split across workgroups when B * T * Hq is small; a combine kernel
-// merges the splits by their log-sum-exp.
+// pairs of b are flattened into M = T * Hq query rows.  A workgroup of eight
+// waves takes one (b, group of 64 query rows, row split) and walks its rows in
+// chunks of 32, each row passing through LDS once:
+//   1. the four score waves copy the chunk's rows from HBM straight into an
+//      LDS ring slot (buffer loads into LDS, NB-1 chunks ahead);
+//   2. S^T = K Q^T: score wave w owns query rows 16w.. against all 32 chunk
+//      rows over the full latent depth, Q held in registers, and runs the
+//      online softmax of its rows alone (base 2, running max moved lazily);
+//      P (bf16) goes to LDS;
+//   3. O[:, dims_u] += P C[:, dims_u]: value wave u owns Dl/4 latent dims of
+//      all 64 query rows; C^T operands come from transposing LDS reads.
+// Steps 2 and 3 of consecutive chunks overlap (a score wave and a value wave
+// share each SIMD).  Rows are split across workgroups when B * T * Hq is
+// small; a combine kernel merges the splits by their log-sum-exp.
 #include "common.hpp"
 
 namespace lsa {
 
-constexpr int kAttWGTarget = 256;   // workgroups the split heuristic aims for
+// Workgroups the split heuristic aims for (one per CU; a compile-time knob).
+#ifndef LSA_ATT_WG_TARGET
+#define LSA_ATT_WG_TARGET 256
+#endif
+constexpr int kAttWGTarget = LSA_ATT_WG_TARGET;
 constexpr int kChunk = 32;          // attended rows per step
 constexpr int kMaxSplitRows = 2048; // most rows one split may take (64 chunks: one per lane)
-constexpr int kMQ = 32;             // query rows per workgroup
+constexpr int64_t kMaxAttendRows = (int64_t)1 << 20;   // per sequence: at most 512 splits
+constexpr int kMQ = 64;             // query rows per workgroup
 constexpr int kAttRing = 4;         // ring slots of kChunk rows
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // keep the running max unless it grows by > 2^8
+// Fourth word of a raw buffer resource (32-bit data format, no swizzle, no
+// stride): the loads below use it with a byte offset and a range of one row.
+constexpr int kBufferWord3 = 0x00020000;
 
 // Row pointer of attended row j of sequence b (nullptr past the end).
 template <typename E>
@@ -109,6 +117,15 @@ __device__ __forceinline__ void lds_barrier() {
 // Parameter order: what the first loads need comes first (14 dwords: the work
 // item, the Q and index addresses, the count pointers), so a build that
 // preloads kernel arguments into scalar registers issues them at launch.
+//
+// Eight waves.  Waves 0..3 ("score waves") stage the rows and compute
+// S^T = K Q^T: score wave w owns query rows 16w .. 16w+15 against every row of
+// a chunk, with its Q fragments in registers, so its rows' online softmax
+// (running max, rescale decision, row sums) needs no other wave.  It publishes
+// P (bf16) and, when its running max moved, the rescale factors.  Waves 4..7
+// ("value waves") compute O += P C: value wave 4+u owns latent dims
+// [u Dl/4, (u+1) Dl/4) of all 64 query rows.  Score wave w and value wave w+4
+// share a SIMD, so one's matrix products overlap the other's LDS traffic.
 template <int Dl, int NB>
 __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     int n_items, int QG, int nsplit, int rows_per_split, int M, int k,
@@ -118,33 +135,33 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     int64_t max_hca, const bf16* __restrict__ latent, const bf16* __restrict__ hca,
     float scale_log2, bf16* __restrict__ out, float* __restrict__ lse, bf16* __restrict__ part_o,
     float* __restrict__ part_lse) {
-    constexpr int NW = 4;                       // compute waves (waves 0..3)
-    constexpr int NP = 4;                       // copy waves (waves 4..7)
+    constexpr int NS = 4;                       // score waves (0..3); value waves are 4..7
     constexpr int SL = Dl / 8;                  // 16-byte slots per latent row
     constexpr int RPI = 64 / SL;                // rows per direct-to-LDS instruction
-    constexpr int IPW = kChunk / (RPI * NP);    // such instructions per copy wave per chunk
-    constexpr int KDT = Dl / 32;                // k-steps of Q K^T
-    constexpr int DPW = Dl / NW;                // latent dims per wave in P C
+    constexpr int IPW = kChunk / (RPI * NS);    // such row groups per score wave per chunk
+    constexpr int CPW = kChunk / NS;            // buffer loads per score wave per chunk
+    constexpr int KDT = Dl / 32;                // k-steps of one S^T tile
+    constexpr int DPW = Dl / 4;                 // latent dims per value wave
     constexpr int NDT = DPW / 16;               // 16-wide dim tiles of P C
-    constexpr int PROW = 40;                    // bf16 per query row of P (conflict-free reads)
-    static_assert(SL >= 16 && IPW >= 1 && NB >= 2 && NB <= 4, "tiling");
-    static_assert(kMQ * DPW * NW <= kChunk * Dl, "output staging fits one ring slot");
+    constexpr int QT = kMQ / 16;                // 16-row query tiles
+    constexpr int PROW = 40;                    // bf16 per query row of P (32 + padding)
+    static_assert(SL >= 16 && IPW >= 1 && NB >= 3 && NB <= 4 && QT == NS, "tiling");
+    static_assert(kMQ * Dl <= NB * kChunk * Dl, "output staging fits the ring");
 
     // One LDS object holds every buffer: the compiler then leaves the ordering of
     // the direct-to-LDS copies and the LDS reads to the explicit counted waits
     // and barriers below instead of draining all copies before each LDS read.
     constexpr int OFF_PBUF = NB * kChunk * Dl * 2;          // ring: NB slots of kChunk rows
-    constexpr int OFF_SMAX = OFF_PBUF + 2 * kMQ * PROW * 2; // P (bf16), two buffers
-    constexpr int OFF_FLAG = OFF_SMAX + 2 * kMQ * 4;        // chunk maxima of the two row tiles
-    constexpr int OFF_ABUF = OFF_FLAG + 32;                 // per-wave "running max moves" flags, two sets
-    constexpr int OFF_ML = OFF_ABUF + kMQ * 4;              // rescale factors of O
+    constexpr int OFF_ABUF = OFF_PBUF + 2 * kMQ * PROW * 2; // P (bf16), two buffers
+    constexpr int OFF_FLAG = OFF_ABUF + 2 * kMQ * 4;        // rescale factors, two buffers
+    constexpr int OFF_ML = OFF_FLAG + 2 * 4 * 4;            // per-query-tile rescale flags, two sets
     constexpr int LDS_BYTES = OFF_ML + 2 * kMQ * 4;         // final (m, l)
+    static_assert(OFF_FLAG % 16 == 0, "flag sets are read as one 16-byte word");
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
     bf16* const ring0 = reinterpret_cast<bf16*>(lds);
     bf16* const pbuf = reinterpret_cast<bf16*>(lds + OFF_PBUF);
-    float (*const smax)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_SMAX);
-    int* const flags = reinterpret_cast<int*>(lds + OFF_FLAG);
     float* const abuf = reinterpret_cast<float*>(lds + OFF_ABUF);
+    int* const flags = reinterpret_cast<int*>(lds + OFF_FLAG);
     float (*const mlbuf)[kMQ] = reinterpret_cast<float (*)[kMQ]>(lds + OFF_ML);
 
     // Work item and per-sequence values.  Every load here is unconditional (a
@@ -165,44 +182,16 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
     const int n16 = lane & 15;
     const int g = lane >> 4;
-    const bool copier = wave >= NW;
-    const int rt = (wave >> 1) & 1;             // Q K^T: chunk rows 16rt .. 16rt+15
-    const int ht = wave & 1;                    //        query rows 16ht .. 16ht+15
+    const bool vwave = wave >= NS;
+    const int u = wave - NS;                    // value wave: dims DPW*u ..
 
     const int rs = split * rows_per_split;
     const int32_t* idx = topk_idx + (int64_t)b * k;
     const int64_t qrow0 = (int64_t)b * M + (int64_t)qg * kMQ;   // first query row of the group
     const int mq = min(kMQ, M - qg * kMQ);                        // valid query rows
 
-    // Q fragments (A operand): query row 16ht + n16, dims 32kk + 8g .. +7
-    bf16x8 qf[KDT];
-    if (!copier) {
-        // rows past the group's end read its first row and are zeroed after
-        const bool ok = 16 * ht + n16 < mq;
-        const bf16* qp = qa + (qrow0 + (ok ? 16 * ht + n16 : 0)) * Dl + 8 * g;
-#pragma unroll
-        for (int kk = 0; kk < KDT; ++kk) qf[kk] = load8(qp + 32 * kk);
-        if (!ok) {
-#pragma unroll
-            for (int kk = 0; kk < KDT; ++kk) qf[kk] = zero8();
-        }
-    }
-    // Copy wave p stages rows 8p .. 8p+7 of every chunk.  Lane c holds the
-    // chosen-entry indices of those rows of chunk c (a split has at most 64
-    // chunks); rows past the split end are clamped to its last row.
-    // The loads are speculative (clamped into the index row, used only for rows
-    // below the top-k count), so they do not wait for the counts; rows past the
-    // split end re-read the split's first row.
-    int ridx[8];
-    int first_idx = 0;
-    if (copier) {
-#pragma unroll
-        for (int j8 = 0; j8 < 8; ++j8)
-            ridx[j8] = idx[min(rs + kChunk * lane + 8 * (wave - NW) + j8, k - 1)];
-        first_idx = idx[min(rs, k - 1)];
-    }
-    // The per-sequence counts and row starts load while the vector loads above
-    // are in flight.
+    // The per-sequence counts and row starts (scalar loads; they overlap the
+    // score waves' first vector loads below).
     const int topk_cnt = topk_count[b];
     const int hca_cnt = hca_count[b];
     const int64_t lrs = latent_row_start[b];
@@ -212,211 +201,185 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     const int n = ntop + nh;
     const int re = min(n, rs + rows_per_split);
     const int nchunks = (active && re > rs) ? (re - rs + kChunk - 1) / kChunk : 0;
-    // Q (compute waves) and the indices (copy waves) are complete before the
-    // loop.  Only the copy waves issue copies, so their counted waits below are
-    // exact, and the compute waves never have a copy outstanding when they read
-    // LDS.
-    wait_vmcnt<0>();
-    // Copy waves: the 64-bit address of every row they stage, computed once
-    // (lane c holds rows 8p .. 8p+7 of chunk c, p = wave - NW), so a copy costs
-    // two lane reads and no branches.  Rows past the split end re-read the
-    // split's first row (finite data, probability zero).
-    uint32_t raddr_lo[8], raddr_hi[8];
-    if (copier) {
-        const uint64_t lat = (uint64_t)latent, hc = (uint64_t)hca;
-#pragma unroll
-        for (int j8 = 0; j8 < 8; ++j8) {
-            const int j0 = rs + kChunk * lane + 8 * (wave - NW) + j8;
-            const bool past = j0 >= re;
-            const int j = past ? rs : j0;
-            const int e = past ? first_idx : ridx[j8];
-            const uint64_t a = j < ntop ? lat + (uint64_t)(lrs + e) * (uint64_t)(Dl * 2)
-                                        : hc + (uint64_t)(hrs + (j - ntop)) * (uint64_t)(Dl * 2);
-            raddr_lo[j8] = (uint32_t)a;
-            raddr_hi[j8] = (uint32_t)(a >> 32);
-        }
-    }
-    f32x4 o[2][NDT];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int nt = 0; nt < NDT; ++nt) o[h2][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // wave 0 also accumulates P . 1: the row sums l of P, rescaled with O
-    f32x4 ol[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    // running max (base 2) and sum of query rows 16ht + 4g + v (sums kept by rt == 0)
-    float m_ref[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        m_ref[v] = -INFINITY;
-    }
 
-    // Chunk c -> ring slot c % NB.  Instruction i of copy wave p moves chunk rows
-    // 8p + RPI*i ..; lane L fills physical slot L % SL of its row r with logical
-    // slot (L % SL) ^ swz(r).  Rows past the split end re-read its first row
-    // (finite data, probability zero).
+    // Score wave w stages rows 8w .. 8w+7 of every chunk: lane c holds the 64-bit
+    // addresses of those rows of chunk c (a split has at most 64 chunks), so a
+    // copy costs two lane reads and no branches.
+    uint32_t raddr_lo[8], raddr_hi[8];
+    // score wave w's Q fragments and whether its query rows exist
+    const bool q_ok = 16 * wave + n16 < mq;
+    bf16x8 qf[KDT];
+
+    // Chunk c -> ring slot c % NB.  Score wave w moves chunk rows 8w .. 8w+7, one
+    // row per buffer load with the row's address as the (wave-uniform) buffer
+    // base; when a row is shorter than the wave (Dl < 512), only the lanes that
+    // cover it are active.  Lane L of an instruction fills LDS 16 bytes at
+    // (instruction base) + 16 L, i.e. physical slot L % SL of row r, with logical
+    // slot (L % SL) ^ swz(r).  Buffer (not flat) loads keep the LDS reads of
+    // these waves on partial lgkmcnt waits: the compiler treats a flat load
+    // into LDS as an unordered LDS access and would drain every LDS read.
+    // Chunks past the split's last are issued too, with an empty buffer range
+    // (the hardware's range check then reads no memory), so every step issues
+    // the same number of copies and the waits are branch-free.
     auto issue_chunk = [&](int c) {
         bf16* slot = ring0 + (c % NB) * (kChunk * Dl);
+        const int range = c < nchunks ? Dl * 2 : 0;
+        const int cl = c & 63;
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {
             const int sub = lane / SL;                     // row of this lane in the instruction
-            const int rbase = 8 * (wave - NW) + RPI * i;
-            const int rl = rbase + sub;
-            uint32_t lo = __builtin_amdgcn_readlane(raddr_lo[RPI * i], c);
-            uint32_t hi = __builtin_amdgcn_readlane(raddr_hi[RPI * i], c);
+            const int rbase = 8 * wave + RPI * i;
 #pragma unroll
-            for (int s2 = 1; s2 < RPI; ++s2)
-                if (sub == s2) {
-                    lo = __builtin_amdgcn_readlane(raddr_lo[RPI * i + s2], c);
-                    hi = __builtin_amdgcn_readlane(raddr_hi[RPI * i + s2], c);
-                }
-            const bf16* row = reinterpret_cast<const bf16*>(((uint64_t)hi << 32) | lo);
-            __builtin_amdgcn_global_load_lds(
-                (const void*)(row + 8 * ((lane % SL) ^ slot_swz(rl))),
-                (__attribute__((address_space(3))) void*)(slot + rbase * Dl), 16, 0, 0);
+            for (int s2 = 0; s2 < RPI; ++s2) {
+                const uint32_t lo = __builtin_amdgcn_readlane(raddr_lo[RPI * i + s2], cl);
+                const uint32_t hi = __builtin_amdgcn_readlane(raddr_hi[RPI * i + s2], cl);
+                void* row = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+                const __amdgpu_buffer_rsrc_t rsrc =
+                    __builtin_amdgcn_make_buffer_rsrc(row, (short)0, range, kBufferWord3);
+                if (RPI == 1 || sub == s2)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rsrc, (__attribute__((address_space(3))) void*)(slot + rbase * Dl), 16,
+                        (uint32_t)(16 * ((lane % SL) ^ slot_swz(rbase + s2))), 0, 0, 0);
+            }
         }
     };
 
+    // Score wave state: running max (base 2) of query row 16w + n16 (the same in
+    // the four lanes of that row), and this lane's share of its row sum.
+    float m_ref = -INFINITY;
+    float l_part = 0.0f;
+
+    // Score wave w, chunk c: S^T tiles (chunk rows 16rt .., query rows 16w ..)
+    // over the full latent depth, then P against the running max into
+    // pbuf[c & 1], and this wave's rescale flag into flags[c & 1][w].
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-    // Q K^T of chunk c, then P against the running max into pbuf[c & 1] and this
-    // wave's "running max must move" flag into flags[c & 1].  Returns the
-    // base-2 logits (kept for the slow path).
-    auto qk_p = [&](int c) -> f32x4 {
+    auto score = [&](int c) {
         const int r0 = rs + c * kChunk;
         const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
-        // S tile: D[4g+v][n16] = query row 16ht + 4g + v against chunk row 16rt + n16
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         {
-            const int r = 16 * rt + n16;
-            const int sw = slot_swz(r);
-            // logical slot 4kk + g sits at physical ((4(kk & 3) + g) ^ sw) + 16(kk >> 2):
-            // the swizzle only touches the low four slot bits, so four base
-            // addresses and immediate offsets cover every step
+            // A operand: chunk row 16rt + n16, dims 32kk + 8g .. +7.  Logical slot
+            // 4kk + g sits at physical ((4(kk & 3) + g) ^ sw) + 16(kk >> 2); the
+            // swizzle depends on the row's low four bits only, so rows r and r+16
+            // share it, and four base addresses plus immediate offsets cover
+            // every step.
+            const int sw = slot_swz(n16);
             const bf16* kp[4];
 #pragma unroll
-            for (int b4 = 0; b4 < 4; ++b4) kp[b4] = sl + r * Dl + 8 * ((4 * b4 + g) ^ sw);
-            // K operands through an 8-deep register window: 8 reads stay in flight
-            constexpr int KW = KDT < 8 ? KDT : 8;
+            for (int b4 = 0; b4 < 4; ++b4) kp[b4] = sl + n16 * Dl + 8 * ((4 * b4 + g) ^ sw);
+            // Steps alternate between the two row tiles and between two partial
+            // accumulators per tile, so four independent product chains are in
+            // flight; reads run KW steps ahead of the products.
+            constexpr int NSTEP = 2 * KDT;
+            constexpr int KW = NSTEP < 16 ? NSTEP : 16;   // reads in flight
+            auto kaddr = [&](int i) {
+                const int rt = i & 1, kk = i >> 1;
+                return reinterpret_cast<const bf16x8*>(kp[kk & 3] + rt * 16 * Dl + 128 * (kk >> 2));
+            };
+            f32x4 acc4[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                             f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
             bf16x8 kb[KW];
 #pragma unroll
-            for (int kk = 0; kk < KW; ++kk)
-                kb[kk] = *reinterpret_cast<const bf16x8*>(kp[kk & 3] + 128 * (kk >> 2));
+            for (int i = 0; i < KW; ++i) kb[i] = *kaddr(i);
 #pragma unroll
-            for (int kk = 0; kk < KDT; ++kk) {
-                sacc = mfma16(qf[kk], kb[kk % KW], sacc);
-                if (kk + KW < KDT)
-                    kb[kk % KW] = *reinterpret_cast<const bf16x8*>(kp[(kk + KW) & 3] + 128 * ((kk + KW) >> 2));
+            for (int i = 0; i < NSTEP; ++i) {
+                acc4[i & 3] = mfma16(kb[i % KW], qf[i >> 1], acc4[i & 3]);
+                if (i + KW < NSTEP) kb[i % KW] = *kaddr(i + KW);
             }
-            // schedule: the first KW reads, then one product per refill read
-            __builtin_amdgcn_sched_group_barrier(0x100, KW, 0);
-#pragma unroll
-            for (int kk = 0; kk < KDT - KW; ++kk) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, KW, 0);
+            sacc[0] = acc4[0] + acc4[2];
+            sacc[1] = acc4[1] + acc4[3];
         }
-        // this lane holds query rows q0 + v (v = 0..3) against chunk row 16rt + n16
-        const int q0 = 16 * ht + 4 * g;
-        const bool valid = r0 + 16 * rt + n16 < re;
-        f32x4 x;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) x[v] = valid ? sacc[v] * scale_log2 : -INFINITY;
-        // Fast path: P against the running max, which stands unless some logit of
-        // the chunk exceeds it by more than kRescaleSlack (lazy rescale; always on
-        // the first chunk, as -inf + slack = -inf).  p <= 2^kRescaleSlack.
-        bf16* pb = pbuf + (c & 1) * (kMQ * PROW);
+        // this lane holds query row 16w + n16 against chunk rows 16rt + 4g + v
+        float x[2][4];
         bool over = false;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            over = over || x[v] > m_ref[v] + kRescaleSlack;
-            const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
-            pb[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
-        }
-        const bool wave_over = __ballot(over) != 0;
-        if (lane == 0) flags[4 * (c & 1) + wave] = wave_over ? 1 : 0;
-        return x;
-    };
-    // After the barrier that publishes chunk c's P and flags: the slow path if
-    // any flag is set, then O[:, dims_w] += P C[:, dims_w].
-    auto pv = [&](int c, f32x4 x) {
-        const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
-        bf16* pb = pbuf + (c & 1) * (kMQ * PROW);
-        const int* fl = flags + 4 * (c & 1);
-        // P C over this wave's dims.  A: query row 16h2 + n16, chunk rows 8g .. 8g+7.
-        // B from transposing reads: in each 16-lane group, lanes 4j..4j+3 point at
-        // chunk row 8g + j (+4 for the upper half), 4 dims each, and lane i receives
-        // dim i of those 4 rows.
-        bf16x8 pa[2];
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-            pa[h2] = *reinterpret_cast<const bf16x8*>(&pb[(16 * h2 + n16) * PROW + 8 * g]);
+            for (int v = 0; v < 4; ++v) {
+                const bool valid = r0 + 16 * rt + 4 * g + v < re;
+                x[rt][v] = valid ? sacc[rt][v] * scale_log2 : -INFINITY;
+                over = over || x[rt][v] > m_ref + kRescaleSlack;
+            }
+        // Lazy rescale: the running max stands unless some logit of the chunk
+        // exceeds it by more than kRescaleSlack (always on the first chunk, as
+        // -inf + slack = -inf), so p <= 2^kRescaleSlack.  Rare: the row maxima are
+        // met across the four lanes of each row, and the factors published.
+        int grew = 0;
+        if (__ballot(over) != 0) {
+            float cm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                             fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            cm = fmaxf(cm, __shfl_xor(cm, 16));
+            cm = fmaxf(cm, __shfl_xor(cm, 32));
+            const bool grow = cm > m_ref + kRescaleSlack;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - cm) : 1.0f;
+            m_ref = grow ? cm : m_ref;
+            l_part *= alpha;
+            if (g == 0) abuf[(c & 1) * kMQ + 16 * wave + n16] = alpha;
+            grew = __ballot(grow) != 0 ? 1 : 0;
+        }
+        bf16* pb = pbuf + (c & 1) * (kMQ * PROW) + (16 * wave + n16) * PROW + 4 * g;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            bf16x4 p4;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const bf16 p = (bf16)(x[rt][v] == -INFINITY ? 0.0f
+                                                            : __builtin_amdgcn_exp2f(x[rt][v] - m_ref));
+                p4[v] = p;
+                l_part += (float)p;                 // the sums use the rounded P that P C uses
+            }
+            *reinterpret_cast<bf16x4*>(pb + 16 * rt) = p4;
+        }
+        if (lane == 0) flags[4 * (c & 1) + wave] = grew;
+    };
+
+    // Value wave u, chunk c (after the barrier that published P(c)): rescale the
+    // O rows whose running max moved, then O[:, dims_u] += P C[:, dims_u].
+    f32x4 o[QT][NDT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int nt = 0; nt < NDT; ++nt) o[qt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto pv = [&](int c) {
+        const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
+        const bf16* pb = pbuf + (c & 1) * (kMQ * PROW);
+        // A: query row 16qt + n16, chunk rows 8g .. 8g+7
+        bf16x8 pa[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            pa[qt] = *reinterpret_cast<const bf16x8*>(&pb[(16 * qt + n16) * PROW + 8 * g]);
+        // B from transposing reads: in each 16-lane group, lanes 4j..4j+3 point at
+        // chunk row 8g + j (+4 for the upper half), 4 dims each, and lane i
+        // receives dim i of those 4 rows.
         const int trow0 = 8 * g + (n16 >> 2);
         const int trow1 = trow0 + 4;
         const int sw0 = slot_swz(trow0), sw1 = slot_swz(trow1);
         const int q4 = n16 & 3;
         const int off = 4 * (q4 & 1);
-        // all of the chunk's C^T operands are read before the products, so the
-        // transposing reads overlap each other rather than the matrix ops
         bf16x4 lo[NDT], hi[NDT];
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) {
-            const int ls = (DPW / 8) * wave + 2 * nt + (q4 >> 1);   // logical 16-byte slot
+            const int ls = (DPW / 8) * u + 2 * nt + (q4 >> 1);   // logical 16-byte slot
             lo[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4*)(sl + trow0 * Dl + 8 * (ls ^ sw0) + off));
             hi[nt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                 (__attribute__((address_space(3))) bf16x4*)(sl + trow1 * Dl + 8 * (ls ^ sw1) + off));
         }
-        // the flags are read with the operands, so their latency overlaps
-        const bool slow = (fl[0] | fl[1] | fl[2] | fl[3]) != 0;   // uniform
-        if (slow) {
-            // Slow path: the chunk maxima of the two row tiles meet, the running
-            // max moves where it grew by more than the slack (alpha = 2^(m_old -
-            // m_new), 0 on the first chunk), and P is recomputed against it.
-            const int q0 = 16 * ht + 4 * g;
-            const bool valid = rs + c * kChunk + 16 * rt + n16 < re;
-            f32x4 cm;
+        const int4 fl = *reinterpret_cast<const int4*>(flags + 4 * (c & 1));
+        const int fl_any = __builtin_amdgcn_readfirstlane(fl.x | fl.y | fl.z | fl.w);
+        if (fl_any) {
+            const int fq[4] = {fl.x, fl.y, fl.z, fl.w};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) cm[v] = group_max<16>(x[v]);
-            if (n16 == 0) *reinterpret_cast<f32x4*>(&smax[rt][q0]) = cm;
-            lds_barrier();
-            const f32x4 ma = *reinterpret_cast<const f32x4*>(&smax[0][q0]);
-            const f32x4 mb = *reinterpret_cast<const f32x4*>(&smax[1][q0]);
-            f32x4 alpha;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const float cmax = fmaxf(ma[v], mb[v]);
-                const bool grow = cmax > m_ref[v] + kRescaleSlack;
-                alpha[v] = grow ? __builtin_amdgcn_exp2f(m_ref[v] - cmax) : 1.0f;
-                m_ref[v] = grow ? cmax : m_ref[v];
-                const float p = valid ? __builtin_amdgcn_exp2f(x[v] - m_ref[v]) : 0.0f;
-                pb[(q0 + v) * PROW + 16 * rt + n16] = (bf16)p;
-            }
-            if (rt == 0 && n16 == 0) *reinterpret_cast<f32x4*>(&abuf[q0]) = alpha;
-            lds_barrier();
-            // rescale O (and wave 0's row sums) rows whose running max moved
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-                const f32x4 al = *reinterpret_cast<const f32x4*>(&abuf[16 * h2 + 4 * g]);
-                if (al[0] != 1.0f || al[1] != 1.0f || al[2] != 1.0f || al[3] != 1.0f) {
+            for (int qt = 0; qt < QT; ++qt) {
+                if (__builtin_amdgcn_readfirstlane(fq[qt])) {
+                    const f32x4 al =
+                        *reinterpret_cast<const f32x4*>(&abuf[(c & 1) * kMQ + 16 * qt + 4 * g]);
 #pragma unroll
                     for (int nt = 0; nt < NDT; ++nt)
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) o[h2][nt][v] *= al[v];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) ol[h2][v] *= al[v];
+                        for (int v = 0; v < 4; ++v) o[qt][nt][v] *= al[v];
                 }
             }
-            // P was rewritten: read the operands again
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2)
-                pa[h2] = *reinterpret_cast<const bf16x8*>(&pb[(16 * h2 + n16) * PROW + 8 * g]);
-        }
-        if (wave == 0) {
-            bf16x8 ones;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.0f;
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) ol[h2] = mfma16(pa[h2], ones, ol[h2]);
         }
 #pragma unroll
         for (int nt = 0; nt < NDT; ++nt) {
@@ -427,169 +390,295 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
                 cb[4 + j] = hi[nt][j];
             }
 #pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) o[h2][nt] = mfma16(pa[h2], cb, o[h2][nt]);
+            for (int qt = 0; qt < QT; ++qt) o[qt][nt] = mfma16(pa[qt], cb, o[qt][nt]);
         }
     };
 
-    // Pipeline, one barrier per chunk (X_c): before it, every compute wave has
-    // published chunk c's P and flag and finished P C of chunk c-1, and the copy
-    // waves have staged chunk c+1; after it, the copy waves refill chunk c-1's
-    // slot with chunk c+NB-1 while the compute waves run P C of chunk c and
-    // Q K^T of chunk c+1.  P and the flags alternate between two buffers, so the
-    // writes for chunk c+1 never meet a late reader of chunk c.  The slow path
-    // adds two barriers, taken by all eight waves (every wave reads the same
-    // flags after X_c).
-    if (copier) {
+    // Pipeline, one barrier per chunk (X_c).  Between X_c and X_{c+1} the value
+    // waves run P C of chunk c while the score waves refill chunk c-1's slot with
+    // chunk c+NB-1 and run S^T and P of chunk c+1.  Before X_c every score wave
+    // has waited for its own copies of chunk c+1, so the barrier certifies the
+    // whole chunk staged; P, the factors and the flags alternate between two
+    // buffers, so the writes for chunk c+1 never meet a late reader of chunk c-1.
+    if (!vwave) {
+        // Every vector load of the score waves sits in this one straight-line
+        // region, so the compiler's own waits track them exactly.  Indices first:
+        // the loads are speculative (clamped into the index row, used only for
+        // rows below the top-k count), so they do not wait for the counts.
+        int ridx[8];
 #pragma unroll
-        for (int c = 0; c < NB - 1; ++c)
-            if (c < nchunks) issue_chunk(c);
-        static_assert(NB <= 4, "the waits below cover two later chunks");
-        // X_{-1}: chunk 0 staged
+        for (int j8 = 0; j8 < 8; ++j8)
+            ridx[j8] = idx[min(rs + kChunk * lane + 8 * wave + j8, k - 1)];
+        const int first_idx = idx[min(rs, k - 1)];
+        __builtin_amdgcn_sched_barrier(0);      // the index loads stay ahead of Q's
+        // Q fragments (B operand of S^T = K Q^T): query row 16w + n16, dims
+        // 32kk + 8g .. +7, in flight while the row addresses are formed.  Rows
+        // past the group's end read its first row and are zeroed before use.
         {
-            const int after = min(nchunks - 1, NB - 2);   // chunks issued after chunk 0
-            if (after >= 2) wait_vmcnt<2 * IPW>();
-            else if (after == 1) wait_vmcnt<IPW>();
-            else wait_vmcnt<0>();
+            const bf16* qp = qa + (qrow0 + (q_ok ? 16 * wave + n16 : 0)) * Dl + 8 * g;
+#pragma unroll
+            for (int kk = 0; kk < KDT; ++kk) qf[kk] = load8(qp + 32 * kk);
         }
-        lds_barrier();
-        for (int c = 0; c < nchunks; ++c) {
-            // chunk c+1 staged before X_c (chunks up to c+NB-2 are issued)
-            const int after = min(nchunks - 1, c + NB - 2) - (c + 1);
-            if (after >= 1) wait_vmcnt<IPW>();
-            else wait_vmcnt<0>();
-            lds_barrier();                                      // X_c
-            if (c + NB - 1 < nchunks) issue_chunk(c + NB - 1);
-            const int* fl = flags + 4 * (c & 1);
-            if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0) {
-                lds_barrier();                                  // slow path: maxima met
-                lds_barrier();                                  // slow path: P republished
+        __builtin_amdgcn_sched_barrier(0);      // ... and Q's ahead of the first wait
+        {
+            // Rows past the split end re-read the split's first row (finite data,
+            // probability zero).  Both candidate addresses, then a select.
+            const uint64_t lat = (uint64_t)latent, hc = (uint64_t)hca;
+#pragma unroll
+            for (int j8 = 0; j8 < 8; ++j8) {
+                const int j0 = rs + kChunk * lane + 8 * wave + j8;
+                const bool past = j0 >= re;
+                const int j = past ? rs : j0;
+                const int e = past ? first_idx : ridx[j8];
+                const uint64_t al = lat + (uint64_t)(lrs + e) * (uint64_t)(Dl * 2);
+                const uint64_t ah = hc + (uint64_t)(hrs + (j - ntop)) * (uint64_t)(Dl * 2);
+                const bool top = j < ntop;
+                raddr_lo[j8] = top ? (uint32_t)al : (uint32_t)ah;
+                raddr_hi[j8] = top ? (uint32_t)(al >> 32) : (uint32_t)(ah >> 32);
             }
         }
-        // the two barriers of the output stage below
-        lds_barrier();
-        lds_barrier();
-        return;
+        // From here on the score waves issue no vector memory operation but the
+        // copies, so the counted waits below are exact.  The value
+        // waves never issue a copy, so their transposing LDS reads never wait for
+        // one.
+#pragma unroll
+        for (int c = 0; c < NB - 1; ++c) issue_chunk(c);
+        wait_vmcnt<(NB - 2) * CPW>();       // chunk 0 staged (and Q, which is older)
+        lds_barrier();                                          // X_{-1}: chunk 0 staged
+        if (!q_ok) {
+#pragma unroll
+            for (int kk = 0; kk < KDT; ++kk) qf[kk] = zero8();
+        }
+        if (nchunks > 0) score(0);
+        for (int c = 0; c < nchunks; ++c) {
+            wait_vmcnt<(NB - 3) * CPW>();   // chunk c+1 staged (chunks up to c+NB-2 issued)
+            lds_barrier();                                      // X_c
+            issue_chunk(c + NB - 1);
+            if (c + 1 < nchunks) score(c + 1);
+        }
+        wait_vmcnt<0>();                    // no copy lands after the loop
+        // the row sum of query row 16w + n16 and its running max, for the value waves
+        float l = l_part + __shfl_xor(l_part, 16);
+        l += __shfl_xor(l, 32);
+        if (g == 0) {
+            mlbuf[0][16 * wave + n16] = m_ref;
+            mlbuf[1][16 * wave + n16] = l;
+        }
+    } else {
+        lds_barrier();                                          // X_{-1}
+        for (int c = 0; c < nchunks; ++c) {
+            lds_barrier();                                      // X_c
+            pv(c);
+        }
     }
-    lds_barrier();                                              // X_{-1}
-    f32x4 xc = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (nchunks > 0) xc = qk_p(0);
-    for (int c = 0; c < nchunks; ++c) {
-        lds_barrier();                                          // X_c
-        pv(c, xc);
-        if (c + 1 < nchunks) xc = qk_p(c + 1);
-    }
+    lds_barrier();                                              // (m, l) published
 
-    // publish (m, l); every wave normalises its O columns and stages them in LDS
-    // (ring slot 0, free now) so the stores to HBM are 16 bytes per lane
-    if (rt == 0 && n16 == 0) {
+    if (vwave) {
+        // normalise this lane's O rows 16qt + 4g + v
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mlbuf[0][16 * ht + 4 * g + v] = m_ref[v];
-    }
-    if (wave == 0 && n16 == 0) {
+        for (int qt = 0; qt < QT; ++qt) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&mlbuf[1][16 * qt + 4 * g]);
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
+            for (int v = 0; v < 4; ++v) {
+                const float inv = l4[v] > 0.0f ? 1.0f / l4[v] : 0.0f;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) mlbuf[1][16 * h2 + 4 * g + v] = ol[h2][v];
-    }
-    lds_barrier();
-    bf16* ost = ring0 + wave * (kMQ * DPW);
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int ql = 16 * h2 + 4 * g + v;
-            const float l = mlbuf[1][ql];
-            const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-#pragma unroll
-            for (int nt = 0; nt < NDT; ++nt) ost[ql * DPW + 16 * nt + n16] = (bf16)(o[h2][nt][v] * inv);
+                for (int nt = 0; nt < NDT; ++nt) o[qt][nt][v] *= inv;
+            }
         }
-    lds_barrier();
-    {
-        constexpr int LPR = DPW / 8;            // lanes per staged query row
-        constexpr int RPS = 64 / LPR;           // query rows per store step
-        bf16* dst_base = (nsplit == 1) ? out + qrow0 * Dl
-                                       : part_o + ((int64_t)(b * nsplit + split) * M +
-                                                   (int64_t)qg * kMQ) * Dl;
+        if (nsplit > 1) {
+            // split partial in fragment order [u][qt][nt][lane][v] (bf16), read back
+            // in the same order by the combine: 8 bytes per lane, 512 per store
+            bf16* dst = part_o + ((int64_t)(b * nsplit + split) * QG + qg) * (int64_t)(kMQ * Dl) +
+                        (int64_t)u * (QT * NDT * 256) + 4 * lane;
+            if (active) {
 #pragma unroll
-        for (int i = 0; i < kMQ / RPS; ++i) {
-            const int ql = RPS * i + lane / LPR;
-            const int c8 = 8 * (lane % LPR);
-            if (active && ql < mq)
-                *reinterpret_cast<bf16x8*>(dst_base + (int64_t)ql * Dl + DPW * wave + c8) =
-                    *reinterpret_cast<const bf16x8*>(ost + ql * DPW + c8);
-        }
-    }
-    if (active && tid < mq) {
-        const float l = mlbuf[1][tid];
-        const float v = l > 0.0f ? (mlbuf[0][tid] + log2f(l)) * kLn2 : -INFINITY;
-        if (nsplit == 1) {
-            if (lse) lse[qrow0 + tid] = v;
+                for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                    for (int nt = 0; nt < NDT; ++nt) {
+                        bf16x4 h;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) h[v] = (bf16)o[qt][nt][v];
+                        *reinterpret_cast<bf16x4*>(dst + (qt * NDT + nt) * 256) = h;
+                    }
+            }
         } else {
-            part_lse[(int64_t)(b * nsplit + split) * M + (int64_t)qg * kMQ + tid] = v;
+            // stage this wave's [kMQ x DPW] block in the (now idle) ring, then store
+            // 16 bytes per lane along the output rows
+            bf16* ost = ring0 + u * (kMQ * DPW);
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+#pragma unroll
+                    for (int nt = 0; nt < NDT; ++nt)
+                        ost[(16 * qt + 4 * g + v) * DPW + 16 * nt + n16] = (bf16)o[qt][nt][v];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_waitcnt(0xc07f);         // lgkmcnt(0): the wave's LDS writes land
+            constexpr int LPR = DPW / 8;                // lanes per staged query row
+            constexpr int RPS = 64 / LPR;               // query rows per store step
+            bf16* dst_base = out + qrow0 * Dl;
+#pragma unroll
+            for (int i = 0; i < kMQ / RPS; ++i) {
+                const int ql = RPS * i + lane / LPR;
+                const int c8 = 8 * (lane % LPR);
+                if (active && ql < mq)
+                    *reinterpret_cast<bf16x8*>(dst_base + (int64_t)ql * Dl + DPW * u + c8) =
+                        *reinterpret_cast<const bf16x8*>(ost + ql * DPW + c8);
+            }
+        }
+    } else if (wave == 0 && active) {
+        const float l = mlbuf[1][lane];
+        const float v = l > 0.0f ? (mlbuf[0][lane] + log2f(l)) * kLn2 : -INFINITY;
+        if (nsplit > 1) {
+            part_lse[((int64_t)(b * nsplit + split) * QG + qg) * kMQ + lane] = v;
+        } else if (lse && lane < mq) {
+            lse[qrow0 + lane] = v;
         }
     }
 }
 
-// Merge the split partials: o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M) per
-// query row; the partial o_s are normalised per split and stored in bf16.
-// A workgroup of 256 threads merges 4 heads; each thread owns 8 dims (16-byte loads).
-constexpr int kCombHeads = 4;
-
-template <typename E>
-__global__ __launch_bounds__(256) void k_attend_combine(int Hq, int Dl, int nsplit, int64_t nbh,
+// Merge the split partials of one (sequence, query group):
+//   o = sum_s e^(lse_s - M) o_s / sum_s e^(lse_s - M),  lse = M + ln(sum_s e^(lse_s - M))
+// per query row (M = the row's largest lse_s).  The partials o_s are normalised
+// per split, bf16, in the attention kernel's fragment order: element
+// [u][qt][nt][lane][v] is query row 16qt + 4(lane/16) + v, latent dim
+// (Dl/4)u + 16nt + lane%16.  A workgroup takes 512 fragments (4 values each) of
+// one 16-row query tile qt, two adjacent ones per thread; its threads issue
+// their loads of a batch of splits before the weights are formed, so the merge
+// costs about one memory round trip plus the bytes.
+template <int Dl, int SB>
+__global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit, int QG, int M,
                                                         const bf16* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
-                                                        E* __restrict__ out,
+                                                        bf16* __restrict__ out,
                                                         float* __restrict__ lse) {
-    extern __shared__ float wsh[];          // [kCombHeads][nsplit] weights
-    __shared__ float tot_sh[kCombHeads];
-    const int wave = threadIdx.x >> 6;      // one head per wave
-    const int lane = threadIdx.x & 63;
-    const int64_t bh = (int64_t)blockIdx.x * kCombHeads + wave;   // (b*T + t)*Hq + h
-    if (bh >= nbh) return;
-    const int h = (int)(bh % Hq);
-    const int64_t bt = bh / Hq;
-    float* w = wsh + wave * nsplit;
-    float M = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, part_lse[(bt * nsplit + s) * Hq + h]);
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float tot = 0.0f;
-    for (int s = lane; s < nsplit; s += 64) {
-        const float ls = part_lse[(bt * nsplit + s) * Hq + h];
-        const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - M);
-        w[s] = wgt;
-        tot += wgt;
+    constexpr int DPW = Dl / 4;
+    constexpr int NDT = DPW / 16;
+    constexpr int QT = kMQ / 16;
+    constexpr int FPT = 4 * NDT * 64;           // fragments of one query tile (all u, nt, lanes)
+    constexpr int WPT = FPT / 512;              // workgroups per query tile (2 fragments a thread)
+    static_assert(FPT % 512 == 0, "fragment blocks");
+    extern __shared__ float wsh[];              // [nsplit][16]: lse, then merge weights
+    __shared__ float red[4][16];
+    __shared__ float rinv[16];
+
+    // Blocks are dealt to XCDs in contiguous ranges, as the attention kernel
+    // deals its items, so a sequence's merge runs on the XCD whose L2 holds the
+    // partials its splits just wrote.
+    const int blk = xcd_item(n_blocks);
+    if (blk < 0) return;
+    const int part = blk % WPT;
+    const int qt = (blk / WPT) % QT;
+    const int bq = blk / (WPT * QT);            // b * QG + qg
+    const int b = bq / QG;
+    const int qg = bq - b * QG;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // this thread's fragments: f and f+1, f = 2(part*256 + tid), over (u, nt,
+    // lane) of tile qt -- adjacent lanes of one tile, so the same four rows and
+    // latent dims d, d+1, one 16-byte load per split
+    const int f = 2 * (part * 256 + tid);
+    const int lanef = f & 63;
+    const int nt = (f >> 6) % NDT;
+    const int u = (f >> 6) / NDT;
+    const int64_t blk_elems = (int64_t)kMQ * Dl;
+    const int64_t frag_off = (int64_t)u * (QT * NDT * 256) + (qt * NDT + nt) * 256 + 4 * lanef;
+    const int64_t split_stride = (int64_t)QG * blk_elems;
+    const bf16* src = part_o + (int64_t)b * nsplit * split_stride + (int64_t)qg * blk_elems + frag_off;
+    const int r4 = 4 * (lanef >> 4);            // the fragments' rows: r4 + j of the tile
+
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // Thread (r = tid % 16, j = tid / 16) forms the weights of row r for splits
+    // j, j+16, ...; the first LS of its lse values load before the partials, so
+    // they do not queue behind them.
+    constexpr int LS = SB >= 32 ? 2 : 1;
+    const float* pl = part_lse + ((int64_t)b * nsplit * QG + qg) * kMQ + 16 * qt;
+    const int r = tid & 15, j = tid >> 4;
+    float lsv[LS];
+#pragma unroll
+    for (int i = 0; i < LS; ++i) lsv[i] = pl[(int64_t)min(j + 16 * i, nsplit - 1) * QG * kMQ + r];
+    __builtin_amdgcn_sched_barrier(0);          // the lse loads stay ahead of the partials
+    // SB loads in flight, unconditional: indices past the last split repeat it
+    // and get no weight
+    bf16x8 v[SB];
+    auto load_batch = [&](int s0) {
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+            v[s] = load8(src + (int64_t)min(s0 + s, nsplit - 1) * split_stride);
+    };
+    auto accumulate = [&](int s0) {
+        const int ns = min(SB, nsplit - s0);
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+            const float4 w4 = *reinterpret_cast<const float4*>(&wsh[(s0 + min(s, ns - 1)) * 16 + r4]);
+            const float wm = s < ns ? 1.0f : 0.0f;
+            const float w[4] = {wm * w4.x, wm * w4.y, wm * w4.z, wm * w4.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                acc[jj] += w[jj] * (float)v[s][jj];
+                acc[4 + jj] += w[jj] * (float)v[s][4 + jj];
+            }
+        }
+    };
+    load_batch(0);
+    __builtin_amdgcn_sched_barrier(0);          // the first batch is in flight during the weights
+    {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < LS; ++i) {
+            const bool ok = j + 16 * i < nsplit;
+            mx = fmaxf(mx, ok ? lsv[i] : -INFINITY);
+            if (ok) wsh[(j + 16 * i) * 16 + r] = lsv[i];
+        }
+        for (int s = j + 16 * LS; s < nsplit; s += 16) {
+            const float ls = pl[(int64_t)s * QG * kMQ + r];
+            wsh[s * 16 + r] = ls;
+            mx = fmaxf(mx, ls);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        if (lane < 16) red[wave][r] = mx;
+        lds_barrier();
+        mx = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+        float tot = 0.0f;
+        for (int s = j; s < nsplit; s += 16) {
+            const float ls = wsh[s * 16 + r];
+            const float w = ls == -INFINITY ? 0.0f : expf(ls - mx);
+            wsh[s * 16 + r] = w;
+            tot += w;
+        }
+        tot += __shfl_xor(tot, 16);
+        tot += __shfl_xor(tot, 32);
+        lds_barrier();                          // every wave has read red[] (maxima)
+        if (lane < 16) red[wave][r] = tot;
+        lds_barrier();
+        if (tid < 16) {
+            tot = (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
+            rinv[r] = tot > 0.0f ? 1.0f / tot : 0.0f;
+            const int ql = 16 * qt + r;
+            if (lse && part == 0 && qg * kMQ + ql < M)
+                lse[(int64_t)b * M + qg * kMQ + ql] = tot > 0.0f ? mx + logf(tot) : -INFINITY;
+        }
+        lds_barrier();                          // weights and 1/sum visible
     }
-    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
-    if (lane == 0 && lse) lse[bh] = tot > 0.0f ? M + logf(tot) : -INFINITY;
-    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    // every lane of the wave wrote its own weights; the wave reads them all
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);     // lgkmcnt(0): LDS writes visible to the wave
-    const int64_t stride = (int64_t)Hq * Dl;
-    for (int d = 8 * lane; d < Dl; d += 8 * 64) {
-        float acc[8];
+    accumulate(0);
+    for (int s0 = SB; s0 < nsplit; s0 += SB) {
+        load_batch(s0);
+        accumulate(s0);
+    }
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const int d = DPW * u + 16 * nt + (lanef & 15);   // even: dims d, d+1
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
-        const bf16* po = part_o + (bt * nsplit * Hq + h) * (int64_t)Dl + d;
-        int s = 0;
-        for (; s + 4 <= nsplit; s += 4) {
-            bf16x8 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = load8(po + (s + u) * stride);
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[j] += w[s + u] * (float)v[u][j];
+    for (int jj = 0; jj < 4; ++jj) {
+        const int ql = 16 * qt + r4 + jj;
+        if (qg * kMQ + ql < M) {
+            bf16x2 h;
+            h[0] = (bf16)(acc[jj] * rinv[r4 + jj]);
+            h[1] = (bf16)(acc[4 + jj] * rinv[r4 + jj]);
+            *reinterpret_cast<bf16x2*>(out + ((int64_t)b * M + qg * kMQ + ql) * Dl + d) = h;
         }
-        for (; s < nsplit; ++s) {
-            const bf16x8 v = load8(po + s * stride);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] += w[s] * (float)v[j];
-        }
-        E* o = out + bh * Dl + d;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = (E)(acc[j] * inv);
     }
 }
 
@@ -693,7 +782,7 @@ size_t lsa_attend_workspace(int dtype, int B, int T, int Hq, int Dl, int k, int6
     if (!attend_mfma_shape(dtype, Hq, Dl)) return 0;
     const AttendPlan p = attend_plan(B, T, Hq, k, max_hca);
     if (p.nsplit <= 1) return 0;
-    const size_t n = (size_t)B * T * p.nsplit * Hq;
+    const size_t n = (size_t)B * p.nsplit * p.QG * kMQ;   // partial query rows
     return n * Dl * sizeof(bf16) + n * sizeof(float);
 }
 
@@ -720,8 +809,9 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
     if (Dl > 1024) return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: Dl=%d > 1024", Dl);
     if (B > 65535 || T > 65535)
         return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: B or T above 65535");
-    if ((int64_t)k + (hca ? max_hca : 0) > (int64_t)1 << 30)
-        return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: too many attended rows");
+    if ((int64_t)k + (hca ? max_hca : 0) > kMaxAttendRows)
+        return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: k + max_hca above %lld rows",
+                    (long long)kMaxAttendRows);
     const int64_t hmax = hca ? max_hca : 0;
     const size_t need = lsa_attend_workspace(dtype, B, T, Hq, Dl, k, hmax);
     if (need > 0 && (!workspace || workspace_bytes < need))
@@ -733,7 +823,7 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
 
     if (attend_mfma_shape(dtype, Hq, Dl)) {
         const AttendPlan p = attend_plan(B, T, Hq, k, hmax);
-        const size_t n = (size_t)B * T * p.nsplit * Hq;
+        const size_t n = (size_t)B * p.nsplit * p.QG * kMQ;
         bf16* part_o = (bf16*)workspace;
         float* part_lse = p.nsplit > 1 ? (float*)(part_o + n * Dl) : nullptr;
         const unsigned grid = (unsigned)(8 * ((p.n_items + 7) / 8));
@@ -754,12 +844,21 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
 #undef LSA_ATT
         rc = launch_status("attend_mfma");
         if (rc != LSA_OK || p.nsplit == 1) return rc;
-        // partials are laid out [b][split][query row]: merge with M = T * Hq rows per b
-        const int64_t nbh = (int64_t)B * M;
-        hipLaunchKernelGGL(k_attend_combine<bf16>,
-                           dim3((unsigned)((nbh + kCombHeads - 1) / kCombHeads)), dim3(256),
-                           sizeof(float) * kCombHeads * p.nsplit, st, M, Dl, p.nsplit, nbh,
-                           part_o, part_lse, (bf16*)out, lse);
+        // partials: one [kMQ x Dl] block per (b, split, query group)
+        const int cblocks = B * p.QG * (kMQ / 16) * (Dl / 128);
+        const unsigned cgrid = (unsigned)(8 * ((cblocks + 7) / 8));
+        const size_t cshm = sizeof(float) * 16 * (size_t)p.nsplit;
+#define LSA_COMB(dl, sb)                                                                       \
+    hipLaunchKernelGGL((k_attend_combine<dl, sb>), dim3(cgrid), dim3(256), cshm, st, cblocks,     \
+                       p.nsplit,                                                               \
+                       p.QG, M, part_o, part_lse, (bf16*)out, lse)
+#define LSA_COMB_DL(sb)                                                                        \
+    if (Dl == 512) LSA_COMB(512, sb); else if (Dl == 256) LSA_COMB(256, sb); else LSA_COMB(128, sb)
+        if (p.nsplit <= 8) { LSA_COMB_DL(8); }
+        else if (p.nsplit <= 16) { LSA_COMB_DL(16); }
+        else { LSA_COMB_DL(32); }
+#undef LSA_COMB_DL
+#undef LSA_COMB
         return launch_status("attend_combine");
     }
     const unsigned blocks = (unsigned)((int64_t)B * T * Hq);

@@ -114,6 +114,8 @@ def test_attend_validation(lib):
     assert f(*a) == -2
     a = list(args); a[15] = float("nan")
     assert f(*a) == -1
+    a = list(args); a[14] = (1 << 20) - 2048 + 1  # k + max_hca above the per-sequence cap
+    assert f(*a) == -2
     need = lib.lsa_workspace_bytes(3, 8, 1, 64, 512, 0, 2048, 3907)
     assert need > 0
     a = list(args); a[19] = need - 1

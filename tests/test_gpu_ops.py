@@ -280,6 +280,30 @@ def test_attend_bf16(ref, B, T, Hq, Dl, lens, counts, hca, k):
     check_attention(o, orf, l, lr)
 
 
+@pytest.mark.parametrize("growth", [0.0, 6.0, 40.0])
+def test_attend_running_max_moves(ref, growth):
+    """Logits that grow along the attended list, so the running maximum moves
+    in later chunks of every split (and by more than any fixed slack)."""
+    S, Hq, Dl = 3000, 64, 512
+    wl = inputs.random_small(311, 1, 1, 4, 32, [S], k=2048, Hq=Hq, Dl=Dl, hca_lens=[900])
+    # latent row i gets a logit offset rising by ~growth over every 64 rows (the
+    # row splits here are 64 rows long, two chunks), along qa's mean direction
+    qa = bf16_to_f64(wl.qa)[0, 0]
+    u = qa.mean(axis=0)
+    u /= np.linalg.norm(u)
+    lat = bf16_to_f64(wl.latent)
+    ramp = growth * (np.arange(S) % 64) / 64
+    wl.latent = inputs.to_bf16_bits((lat + ramp[:, None] * u[None, :] * np.sqrt(Dl)).astype(np.float32))
+    hca = bf16_to_f64(wl.hca)
+    wl.hca = inputs.to_bf16_bits((hca + growth * u[None, :] * np.sqrt(Dl)).astype(np.float32))
+    rng = np.random.default_rng(5)
+    idx, cnt = _random_indices(rng, wl.seq_len, wl.k, [2048])
+    announce(f"attend running max moves growth={growth}")
+    o, l = _attend_gpu(wl, idx, cnt)
+    orf, lr = _attend_ref(ref, wl, idx, cnt)
+    check_attention(o, orf, l, lr)
+
+
 def test_attend_all_selected_equals_dense(ref):
     """Every entry kept, k >= S, no HCA: sparse attention is dense attention (torch, fp64)."""
     S, Hq, Dl = 700, 64, 512
