@@ -28,6 +28,18 @@ constexpr int kScoreRing = 4;          // LDS ring slots per wave (decode kernel
 constexpr int kNonTemporal = 2;
 constexpr int kScoreGroupsPerWave = 32;
 
+// Fourth word of a raw buffer resource (32-bit data format, no swizzle, no
+// stride), for buffer loads into LDS with byte offsets.
+constexpr int kBufferWord3Score = 0x00020000;
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations retire,
+// then s_barrier; outstanding global loads (copies of later data) stay in
+// flight across it.
+__device__ __forceinline__ void lds_barrier_score() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0), vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+}
+
 // vmcnt(n) with the other counters left alone (n <= 63).  Stores count too, so
 // waiting on loads by this bound is conservative.
 template <int N>
@@ -158,11 +170,30 @@ __global__ __launch_bounds__(256) void k_score_decode(
 // ------------------------------------------------------------------ burst
 // Workgroup = 4 waves x 64 entries of one sequence; it walks all T positions.
 // Keys of the wave's 64 entries stay in registers as B operands (32x32x16,
-// two entry tiles); the queries of position t (H <= 64 heads x D) are staged
-// in LDS once per workgroup, double-buffered, rows XOR-swizzled by 16-byte
-// chunk so the 32 heads read by one instruction hit distinct banks.
-template <int KS>
-__global__ __launch_bounds__(256) void k_score_burst(
+// two entry tiles).  The queries and weights of each position (H <= 64 heads x
+// D) are copied from HBM straight into an LDS ring of kBurstRing positions by
+// buffer loads into LDS, kBurstRing-1 positions ahead of use, so their latency
+// hides behind the matrix work of the positions before.  Query rows are
+// XOR-swizzled by 16-byte chunk (applied on the source side of the copies) so
+// the 32 heads read by one instruction hit distinct banks.  Head rows >= H are
+// zero: their copies fall outside the buffer range and the ring starts zeroed.
+// Compile-time knobs: ring depth (positions) and workgroups per CU.  With 3
+// slots of 16 KiB the workgroup holds ~49 KiB of LDS and 142 VGPRs per lane, so
+// three workgroups share a CU (three waves per SIMD).
+#ifndef LSA_BURST_RING
+#define LSA_BURST_RING 3
+#endif
+#ifndef LSA_BURST_MINB
+#define LSA_BURST_MINB 3
+#endif
+constexpr int kBurstRing = LSA_BURST_RING;
+constexpr int kBurstWaves = 4;                           // waves per workgroup
+constexpr int kBurstTiles = 2;                           // 32-entry tiles per wave
+constexpr int kBurstEntries = 32 * kBurstWaves * kBurstTiles;   // entries per workgroup (256)
+constexpr int kBurstMinBlocks = LSA_BURST_MINB;          // workgroups per CU
+
+template <int KS, int NW, int NT, int MINB>
+__global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
     const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int T, int H,
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
@@ -170,97 +201,118 @@ __global__ __launch_bounds__(256) void k_score_burst(
     constexpr int D = 16 * KS;
     constexpr int CH = D / 8;                 // 16-byte chunks per query row
     constexpr int QCHUNKS = 64 * CH;          // per position (64 head slots)
-    __shared__ bf16x8 sq[2][QCHUNKS];
-    __shared__ float sw[2][64];
+    constexpr int NQ = kBurstRing;
+    constexpr int IPQ = QCHUNKS / 64 / NW;    // query copies per wave per position
+    constexpr int CPP = IPQ + 1;              // copies per wave per position (+ the weights)
+    static_assert(IPQ >= 1 && NQ >= 2, "tiling");
+    // one LDS object: NQ query slots, then NQ weight slots
+    __shared__ __attribute__((aligned(16))) unsigned char lds[NQ * QCHUNKS * 16 + NQ * 64 * 4];
+    bf16x8* const sq = reinterpret_cast<bf16x8*>(lds);
+    float* const sw = reinterpret_cast<float*>(lds + NQ * QCHUNKS * 16);
 
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int64_t S = min((int64_t)seq_len[b], max_len);
-    const int64_t e_blk = (int64_t)blockIdx.x * 256;
+    constexpr int EPW = 32 * NT;              // entries per wave
+    const int64_t e_blk = (int64_t)blockIdx.x * (NW * EPW);
     if (e_blk >= S) return;
     const int n32 = lane & 31;
     const int g = lane >> 5;
 
-    // B operands: this wave's two tiles of 32 entries.
-    bf16x8 kb[2][KS];
-    int64_t ent[2];
+    // B operands: this wave's NT tiles of 32 entries.
+    bf16x8 kb[NT][KS];
+    int64_t ent[NT];
     const bf16* kbase = keys + key_row_start[b] * D + 8 * g;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        ent[nt] = e_blk + wave * 64 + nt * 32 + n32;
+    for (int nt = 0; nt < NT; ++nt) {
+        ent[nt] = e_blk + wave * EPW + nt * 32 + n32;
         const int64_t row = ent[nt] < S ? ent[nt] : e_blk;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) kb[nt][ks] = load8(kbase + row * D + 16 * ks);
     }
 
-    // Query staging: QCHUNKS 16-byte chunks per position, spread over 256 threads.
-    constexpr int PER = (QCHUNKS + 255) / 256;
-    bf16x8 qreg[PER];
-    float wreg = 0.0f;
-    auto fetch_q = [&](int t) {
-        const bf16* qt = q + ((int64_t)b * T + t) * H * D;
+    // Padded head rows (and weights) must read as zero: clear the ring once.
+    if (H < 64) {
+        for (int i = tid; i < NQ * QCHUNKS; i += 64 * NW) sq[i] = zero8();
+        for (int i = tid; i < NQ * 64; i += 64 * NW) sw[i] = 0.0f;
+    }
+    lds_barrier_score();
+
+    // Copies of position t into ring slot t % NQ.  Lane L of query copy i of wave
+    // wv fills LDS chunk p = (IPQ wv + i) 64 + L: head h = p / CH, physical chunk
+    // p % CH, which holds logical chunk (p % CH) ^ (h % CH).  The weights take one
+    // 4-byte copy per lane (every wave issues it, so all waves count alike).
+    // Positions past T are issued with an empty range: no memory is read.
+    auto issue = [&](int t) {
+        const int slot = t % NQ;
+        const bool live = t < T;
+        const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + ((int64_t)b * T + (live ? t : 0)) * H * D), (short)0,
+            live ? H * D * 2 : 0, kBufferWord3Score);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + 256 * i;
-            const int h = c / CH, ch = c % CH;
-            qreg[i] = (c < QCHUNKS && h < H) ? load8(qt + (int64_t)h * D + 8 * ch) : zero8();
+        for (int i = 0; i < IPQ; ++i) {
+            const int p0 = (IPQ * wave + i) * 64;
+            const int p = p0 + lane;
+            const int h = p / CH, pc = p % CH;
+            const uint32_t off = (uint32_t)(h * D + 8 * (pc ^ (h & (CH - 1)))) * 2;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                qr, (__attribute__((address_space(3))) void*)(sq + slot * QCHUNKS + p0), 16, off, 0,
+                0, 0);
         }
-        if (tid < 64) wreg = tid < H ? w[((int64_t)b * T + t) * H + tid] : 0.0f;
-    };
-    auto stage_q = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int c = tid + 256 * i;
-            if (c < QCHUNKS) {
-                const int h = c / CH, ch = c % CH;
-                sq[buf][h * CH + (ch ^ (h & (CH - 1)))] = qreg[i];
-            }
-        }
-        if (tid < 64) sw[buf][tid] = wreg;
+        const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(w + ((int64_t)b * T + (live ? t : 0)) * H), (short)0, live ? H * 4 : 0,
+            kBufferWord3Score);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (__attribute__((address_space(3))) void*)(sw + slot * 64), 4, (uint32_t)(4 * lane), 0,
+            0, 0);
     };
 
-    float mx[2] = {-INFINITY, -INFINITY};
+    float mx[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mx[nt] = -INFINITY;
     const int64_t eo = entry_start[b];
-    fetch_q(0);
-    stage_q(0);
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NQ - 1; ++t) issue(t);
     for (int t = 0; t < T; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < T) fetch_q(t + 1);
-        f32x16 acc[2][2];
+        const int slot = t % NQ;
+        wait_vmcnt_score<(NQ - 2) * CPP>();   // position t landed (later ones may be in flight)
+        lds_barrier_score();                  // ... for every wave; all are done with t-1
+        issue(t + NQ - 1);                    // into t-1's slot
+        const bf16x8* qs = sq + slot * QCHUNKS;
+        // The two 32-head halves one after the other: half the accumulators live
+        // at a time, which leaves room for three waves per SIMD, so one wave's
+        // epilogue arithmetic overlaps another's matrix products.
+        float s[NT];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int nt = 0; nt < NT; ++nt) s[nt] = 0.0f;
+#pragma unroll 1
+        for (int mt = 0; mt < 2; ++mt) {
+            f32x16 acc[NT];
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[mt][nt][v] = 0.0f;
+                for (int v = 0; v < 16; ++v) acc[nt][v] = 0.0f;
+            const int h = 32 * mt + n32;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const int h = 32 * mt + n32;
+            for (int ks = 0; ks < KS; ++ks) {
                 const int ch = 2 * ks + g;
-                const bf16x8 a = sq[buf][h * CH + (ch ^ (h & (CH - 1)))];
+                const bf16x8 a = qs[h * CH + (ch ^ (h & (CH - 1)))];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma32(a, kb[nt][ks], acc[mt][nt]);
+                for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma32(a, kb[nt][ks], acc[nt]);
             }
-        }
-        float s[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const f32x4 wq = *reinterpret_cast<const f32x4*>(&sw[buf][32 * mt + 8 * j + 4 * g]);
+                const f32x4 wq = *reinterpret_cast<const f32x4*>(&sw[slot * 64 + 32 * mt + 8 * j + 4 * g]);
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
+                for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        s[nt] += wq[v] * fmaxf(acc[mt][nt][4 * j + v], 0.0f);
+                    for (int v = 0; v < 4; ++v) s[nt] += wq[v] * fmaxf(acc[nt][4 * j + v], 0.0f);
             }
+        }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < NT; ++nt) {
             s[nt] += __shfl_xor(s[nt], 32);
             const float z = s[nt] + bias;
             if (reduce_max) {
@@ -271,12 +323,11 @@ __global__ __launch_bounds__(256) void k_score_burst(
                 if (prob_out) prob_out[o] = sigmoidf(z);
             }
         }
-        if (t + 1 < T) stage_q(buf ^ 1);
-        __syncthreads();
     }
+    wait_vmcnt_score<0>();                    // no copy lands after the workgroup ends
     if (reduce_max && g == 0) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int nt = 0; nt < NT; ++nt)
             if (ent[nt] < S) {
                 z_out[eo + ent[nt]] = mx[nt];
                 if (prob_out) prob_out[eo + ent[nt]] = sigmoidf(mx[nt]);
@@ -391,15 +442,19 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
         return launch_status("score_decode");
     }
     if (mfma_shape) {
-        dim3 grid((unsigned)ceil_div(max_len, 256), (unsigned)B);
+        // 4 waves x 64 entries per workgroup, three workgroups per CU: the waves
+        // sharing a SIMD overlap one another's epilogues with the matrix work.
+        dim3 grid((unsigned)ceil_div(max_len, kBurstEntries), (unsigned)B);
         if (D == 128)
-            hipLaunchKernelGGL(k_score_burst<8>, grid, dim3(256), 0, st, (const bf16*)keys,
-                               key_row_start, seq_len, entry_start, T, H, max_len, (const bf16*)q,
-                               w, bias, reduce_max, z_out, prob_out);
+            hipLaunchKernelGGL((k_score_burst<8, kBurstWaves, kBurstTiles, kBurstMinBlocks>), grid,
+                               dim3(64 * kBurstWaves), 0, st, (const bf16*)keys, key_row_start,
+                               seq_len, entry_start, T, H, max_len, (const bf16*)q, w, bias,
+                               reduce_max, z_out, prob_out);
         else
-            hipLaunchKernelGGL(k_score_burst<4>, grid, dim3(256), 0, st, (const bf16*)keys,
-                               key_row_start, seq_len, entry_start, T, H, max_len, (const bf16*)q,
-                               w, bias, reduce_max, z_out, prob_out);
+            hipLaunchKernelGGL((k_score_burst<4, kBurstWaves, kBurstTiles, kBurstMinBlocks>), grid,
+                               dim3(64 * kBurstWaves), 0, st, (const bf16*)keys, key_row_start,
+                               seq_len, entry_start, T, H, max_len, (const bf16*)q, w, bias,
+                               reduce_max, z_out, prob_out);
         return launch_status("score_burst");
     }
     dim3 grid((unsigned)ceil_div(max_len, 256), (unsigned)B);

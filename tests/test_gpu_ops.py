@@ -98,6 +98,20 @@ def test_score_burst_matrix_path(ref, T, lens, shared):
         check_scores(z, zr, p)
 
 
+@pytest.mark.parametrize("T,H,D,lens", [
+    (8, 48, 128, [700, 129]),      # padded head rows of the query ring
+    (3, 20, 64, [300, 1, 513]),
+    (70, 64, 128, [256]),          # more positions than ring slots, one workgroup
+])
+def test_score_burst_head_shapes(ref, T, H, D, lens):
+    wl = inputs.random_small(31 * H + T, len(lens), T, H, D, lens, bias=-3.0)
+    for reduce_max in (False, True):
+        announce(f"score burst T={T} H={H} D={D} lens={lens} reduce={reduce_max}")
+        z, p = _score_gpu(wl, reduce_max)
+        zr, _ = _score_ref(ref, wl, reduce_max)
+        check_scores(z, zr, p)
+
+
 def test_score_vector_bf16(ref):
     wl = inputs.random_small(5, 2, 2, 5, 24, [333, 90], bias=-0.5)
     for reduce_max in (False, True):
