@@ -35,6 +35,7 @@ int lsa_ref_index_score(const void* keys, int dtype, const int64_t* key_row_star
                         double* z_out, double* prob_out) {
     if (!keys || !key_row_start || !seq_len || !entry_start || !q || !w || !z_out) return -1;
     if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || !dtype_ok(dtype)) return -1;
+    if (reduce_max < 0 || reduce_max > 2) return -1;
 
     for (int b = 0; b < B; ++b) {
         const int64_t S = seq_len[b];
@@ -62,9 +63,40 @@ int lsa_ref_index_score(const void* keys, int dtype, const int64_t* key_row_star
                 }
             }
             if (reduce_max) {
+                /* TS 2.4 OR-mode over indexers: keep the larger of the union so far
+                 * and this indexer's maximum (a NaN on either side yields the other) */
+                const double prev = z_out[entry_start[b] + s];
+                if (reduce_max == 2 && (isnan(m) || prev > m)) m = prev;
                 z_out[entry_start[b] + s] = m;
                 if (prob_out) prob_out[entry_start[b] + s] = 1.0 / (1.0 + exp(-m));
             }
+        }
+    }
+    return 0;
+}
+
+/* O1b -- TS 2.1 "Tiered Selection" (native indexer inside the fetched subset),
+ * TS 2.3 (frozen compressed keys); no bias and no sigmoid in this reading. */
+int lsa_ref_index_rescore(const void* keys, int dtype, const int64_t* key_row_start,
+                          const int64_t* entry_start, const int32_t* cand_idx,
+                          const int32_t* cand_count, int B, int H, int D,
+                          const void* q, const float* w, double* r_out) {
+    if (!keys || !key_row_start || !entry_start || !cand_idx || !cand_count || !q || !w || !r_out)
+        return -1;
+    if (B <= 0 || H <= 0 || D <= 0 || !dtype_ok(dtype)) return -1;
+    for (int b = 0; b < B; ++b) {
+        for (int32_t j = 0; j < cand_count[b]; ++j) {
+            const int32_t s = cand_idx[entry_start[b] + j];
+            const int64_t krow = (key_row_start[b] + s) * (int64_t)D;
+            double r = 0.0;
+            for (int h = 0; h < H; ++h) {
+                const int64_t qrow = ((int64_t)b * H + h) * (int64_t)D;
+                double dot = 0.0;
+                for (int d = 0; d < D; ++d)
+                    dot += load_elem(q, dtype, qrow + d) * load_elem(keys, dtype, krow + d);
+                r += (double)w[(int64_t)b * H + h] * (dot < 0.0 ? 0.0 : dot);   /* ReLU gate */
+            }
+            r_out[entry_start[b] + s] = r;
         }
     }
     return 0;

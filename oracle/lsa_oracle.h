@@ -39,12 +39,31 @@ extern "C" {
  * reduce_max = 1: z_out holds m[b,s] = max_t z[b,t,s] at entry_start[b]+s
  *                 (TS 2.4: union of gates = gate on the maximum logit);
  *                 prob_out, if given, holds sigmoid(m).
+ * reduce_max = 2: as 1, but z_out already holds the union of other indexers
+ *                 (the several layers of TS 2.4, "OR-mode") and receives
+ *                 max(z_out, m); prob_out, if given, holds sigmoid of that.
  * prob_out may be NULL.  Returns 0, or -1 on a bad argument. */
 int lsa_ref_index_score(const void* keys, int dtype, const int64_t* key_row_start,
                         const int32_t* seq_len, const int64_t* entry_start,
                         int B, int T, int H, int D,
                         const void* q, const float* w, double bias, int reduce_max,
                         double* z_out, double* prob_out);
+
+/* O1b Native re-score of the kept subset (TS 2.1 "Tiered Selection": inside
+ * the fetched subset the backbone's native Lightning Indexer takes a
+ * fine-grained top-k; TS 2.3: the compressed indexer keys are the frozen
+ * keys K_IComp, shared with the Memory Indexer).  This build's reading: the
+ * native indexer scores a candidate with its own per-step queries q' and
+ * weights w' against the same key rows, as a plain ranking logit (no bias,
+ * no sigmoid):
+ *   r[b,s] = sum_h w'[b,h] * max(0, sum_d q'[b,h,d] * k[b,s,d])
+ * for every candidate s = cand_idx[entry_start[b]+j], j < cand_count[b],
+ * written at r_out[entry_start[b]+s]; other elements of r_out are untouched.
+ * q': [B,H,D] (same dtype as keys); w': [B,H] fp32.  Returns 0 or -1. */
+int lsa_ref_index_rescore(const void* keys, int dtype, const int64_t* key_row_start,
+                          const int64_t* entry_start, const int32_t* cand_idx,
+                          const int32_t* cand_count, int B, int H, int D,
+                          const void* q, const float* w, double* r_out);
 
 /* O2  Dynamic fetching (TS 2.1 "Dynamic Fetching": every entry whose score
  * reaches 0.5 is kept, with no fixed count).  Since sigmoid(z) >= 0.5 exactly

@@ -46,8 +46,9 @@ def _bind(path):
     lib.lsa_ref_select.argtypes = [P, P, P, I, D, P, P]
     lib.lsa_ref_topk.argtypes = [P, P, P, I, P, P, I, P, P]
     lib.lsa_ref_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, D, P, P]
+    lib.lsa_ref_index_rescore.argtypes = [P, I, P, P, P, P, I, I, I, P, P, P]
     for f in (lib.lsa_ref_index_score, lib.lsa_ref_select, lib.lsa_ref_topk,
-              lib.lsa_ref_sparse_attend):
+              lib.lsa_ref_sparse_attend, lib.lsa_ref_index_rescore):
         f.restype = ctypes.c_int
     return lib
 
@@ -116,8 +117,11 @@ def _check(rc, name):
 
 
 def index_score(keys, key_row_start, seq_len, entry_start, q, w, bias, reduce_max=False,
-                want_prob=True):
-    """O1: z (and sigmoid) per (b,t,s), or the max over t when reduce_max."""
+                want_prob=True, union_with=None):
+    """O1: z (and sigmoid) per (b,t,s), or the max over t when reduce_max.
+
+    union_with (implies reduce_max): the union logits of other indexers; the
+    result is their elementwise max with this indexer's max over t (OR-mode)."""
     lib = _load()
     keys = np.ascontiguousarray(keys)
     q = np.ascontiguousarray(q)
@@ -130,15 +134,45 @@ def index_score(keys, key_row_start, seq_len, entry_start, q, w, bias, reduce_ma
     entry_start = _c(entry_start, np.int64)
     w = _c(w, np.float32)
     assert w.shape == (B, T, H)
+    mode = 2 if union_with is not None else (1 if reduce_max else 0)
     n_out = int(max(int(entry_start[b]) + int(seq_len[b]) for b in range(B)))
-    n_out = n_out * (1 if reduce_max else T)
-    z = np.full(n_out, np.nan, dtype=np.float64)
+    n_out = n_out * (1 if mode else T)
+    if union_with is not None:
+        z = np.array(union_with, dtype=np.float64, copy=True)
+        assert z.shape == (n_out,)
+    else:
+        z = np.full(n_out, np.nan, dtype=np.float64)
     prob = np.full(n_out, np.nan, dtype=np.float64) if want_prob else None
     rc = lib.lsa_ref_index_score(_ptr(keys), dt, _ptr(key_row_start), _ptr(seq_len),
                                  _ptr(entry_start), B, T, H, D, _ptr(q), _ptr(w), float(bias),
-                                 1 if reduce_max else 0, _ptr(z), _ptr(prob))
+                                 mode, _ptr(z), _ptr(prob))
     _check(rc, "index_score")
     return z, prob
+
+
+def index_rescore(keys, key_row_start, entry_start, cand_idx, cand_count, q, w, r_init=None):
+    """O1b: native re-score of each sequence's candidates (no bias, no sigmoid),
+    scattered to r[entry_start[b] + s]; other elements keep r_init (NaN by default)."""
+    lib = _load()
+    keys = np.ascontiguousarray(keys)
+    q = np.ascontiguousarray(q)
+    dt = _dtype_code(keys)
+    assert _dtype_code(q) == dt, "q and keys must share a dtype"
+    B, H, D = q.shape
+    assert keys.shape[1] == D
+    key_row_start = _c(key_row_start, np.int64)
+    entry_start = _c(entry_start, np.int64)
+    cand_idx = _c(cand_idx, np.int32)
+    cand_count = _c(cand_count, np.int32)
+    w = _c(w, np.float32)
+    assert w.shape == (B, H)
+    n = len(cand_idx)
+    r = np.full(n, np.nan, np.float64) if r_init is None else np.array(r_init, np.float64)
+    rc = lib.lsa_ref_index_rescore(_ptr(keys), dt, _ptr(key_row_start), _ptr(entry_start),
+                                   _ptr(cand_idx), _ptr(cand_count), B, H, D, _ptr(q), _ptr(w),
+                                   _ptr(r))
+    _check(rc, "index_rescore")
+    return r
 
 
 def select(z, entry_start, seq_len, threshold=0.0):

@@ -33,6 +33,13 @@ MUTANTS = {
     "hca_dropped": ("const int32_t nh = hca ? hca_count[b] : 0;", "const int32_t nh = 0;"),
     "hca_row_offset": ("row_off[nt + i] = (hca_row_start[b] + i) * (int64_t)Dl;",
                        "row_off[nt + i] = (hca_row_start[b]) * (int64_t)Dl;"),
+    "rescore_no_relu": ("(dot < 0.0 ? 0.0 : dot)", "dot"),
+    "rescore_weight_of_head_only": ("r += (double)w[(int64_t)b * H + h] *", "r += (double)w[h] *"),
+    "rescore_row_by_position": ("const int64_t krow = (key_row_start[b] + s) * (int64_t)D;\n            double r",
+                                "const int64_t krow = (key_row_start[b] + j) * (int64_t)D;\n            double r"),
+    "union_drops_previous": ("if (reduce_max == 2 && (isnan(m) || prev > m)) m = prev;", ""),
+    "union_takes_min": ("if (reduce_max == 2 && (isnan(m) || prev > m)) m = prev;",
+                        "if (reduce_max == 2 && (isnan(m) || prev < m)) m = prev;"),
 }
 
 

@@ -354,3 +354,104 @@ def test_topk_nan_ranks_last_and_signed_zero_ties(ref):
     for k, w in want.items():
         t, tc = ref.topk(r, es, lens, cand, cnt, k)
         assert t[0, :tc[0]].tolist() == w, k
+
+
+# ------------------------------------------- native re-score of the subset (O1b)
+
+def _cands(rng, lens, frac=0.4):
+    es = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    cand = np.full(int(np.sum(lens)), -1, np.int32)
+    cnt = np.zeros(len(lens), np.int32)
+    for b, S in enumerate(lens):
+        c = np.flatnonzero(rng.random(S) < frac).astype(np.int32)
+        cand[es[b]:es[b] + len(c)] = c
+        cnt[b] = len(c)
+    return es, cand, cnt
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_rescore_matches_score_at_candidates(ref, seed):
+    """On the candidates, the native re-score is the one-position score without bias."""
+    rng = np.random.default_rng(300 + seed)
+    B, H, D = 3, 5, 12
+    lens = np.array([40, 0, 23], np.int32)
+    keys = rng.standard_normal((int(lens.sum()), D)).astype(np.float32)
+    krs = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
+    q = rng.standard_normal((B, H, D)).astype(np.float32)
+    w = rng.uniform(-1, 1, (B, H)).astype(np.float32)
+    es, cand, cnt = _cands(rng, lens)
+    r = ref.index_rescore(keys, krs, es, cand, cnt, q, w)
+    z, _ = ref.index_score(keys, krs, lens, es, q[:, None], w[:, None], 0.0, want_prob=False)
+    for b in range(B):
+        s = cand[es[b]:es[b] + cnt[b]]
+        np.testing.assert_array_equal(r[es[b] + s], z[es[b] + s])
+
+
+def test_rescore_relu_identities(ref):
+    """r(q) - r(-q) = sum_h w_h <q_h,k> and r(q) + r(-q) = sum_h w_h |<q_h,k>| (numpy matmul)."""
+    rng = np.random.default_rng(41)
+    H, D, S = 7, 16, 60
+    keys = rng.standard_normal((S, D)).astype(np.float32)
+    q = rng.standard_normal((1, H, D)).astype(np.float32)
+    w = rng.uniform(0, 2, (1, H)).astype(np.float32)
+    es, cand, cnt = _cands(rng, np.array([S], np.int32), 0.5)
+    args = (keys, np.zeros(1, np.int64), es, cand, cnt)
+    rp = ref.index_rescore(*args, q, w)
+    rm = ref.index_rescore(*args, -q, w)
+    s = cand[:cnt[0]]
+    x = keys.astype(np.float64) @ q[0].astype(np.float64).T          # [S, H] dots
+    lin = x @ w[0].astype(np.float64)
+    absv = np.abs(x) @ w[0].astype(np.float64)
+    assert np.abs((rp - rm)[s] - lin[s]).max() < 1e-12
+    assert np.abs((rp + rm)[s] - absv[s]).max() < 1e-12
+
+
+def test_rescore_touches_only_candidates(ref):
+    rng = np.random.default_rng(43)
+    lens = np.array([30, 17], np.int32)
+    D, H = 8, 3
+    keys = rng.standard_normal((int(lens.sum()), D)).astype(np.float32)
+    krs = np.array([0, 30], np.int64)
+    q = rng.standard_normal((2, H, D)).astype(np.float32)
+    w = np.zeros((2, H), np.float32)
+    es, cand, cnt = _cands(rng, lens, 0.3)
+    init = np.full(int(lens.sum()), -7.0)
+    r = ref.index_rescore(keys, krs, es, cand, cnt, q, w, r_init=init)
+    mask = np.zeros(int(lens.sum()), bool)
+    for b in range(2):
+        mask[es[b] + cand[es[b]:es[b] + cnt[b]]] = True
+    assert np.all(r[~mask] == -7.0)
+    assert np.all(r[mask] == 0.0)          # zero weights: every candidate scores 0
+
+
+# ------------------------------------------- OR-mode union over indexers (O1, TS 2.4)
+
+@pytest.mark.parametrize("seed", range(4))
+def test_union_over_indexers(ref, seed):
+    """Combining indexers keeps the elementwise max; its gate is the OR of their gates."""
+    rng = np.random.default_rng(500 + seed)
+    B, T, H, D = 2, 3, 4, 10
+    lens = np.array([25, 9], np.int32)
+    krs = np.array([0, 25], np.int64)
+    es = krs.copy()
+    zs, union = [], None
+    for layer in range(3):
+        keys = rng.standard_normal((34, D)).astype(np.float32)
+        q = rng.standard_normal((B, T, H, D)).astype(np.float32)
+        w = rng.uniform(0, 1, (B, T, H)).astype(np.float32)
+        bias = float(rng.uniform(-3, 1))
+        z, _ = ref.index_score(keys, krs, lens, es, q, w, bias, reduce_max=True, want_prob=False)
+        zs.append(z)
+        if union is None:
+            union = z
+            prob = None
+        else:
+            union, prob = ref.index_score(keys, krs, lens, es, q, w, bias, union_with=union)
+    np.testing.assert_array_equal(union, np.maximum(np.maximum(zs[0], zs[1]), zs[2]))
+    assert np.abs(prob - 1.0 / (1.0 + np.exp(-union))).max() < 1e-15
+    cu, cnu = ref.select(union, es, lens)
+    for b in range(B):
+        gate_or = np.zeros(lens[b], bool)
+        for z in zs:
+            gate_or |= z[es[b]:es[b] + lens[b]] >= 0.0
+        assert cu[es[b]:es[b] + cnu[b]].tolist() == np.flatnonzero(gate_or).tolist()
