@@ -2,7 +2,9 @@
 
 One step = one pass of the whole path over one batch: index score (max over
 positions) -> gate + compaction -> top-k -> sparse attention, all enqueued on
-one stream.  The default workload is 8 sequences at 500K tokens (125000
+one stream.  Also timed, outside the step: the native indexer's per-step
+re-score of the kept entries with its top-k, and the OR-mode union of three
+indexers (three score launches).  The default workload is 8 sequences at 500K tokens (125000
 compressed entries each, 3907 HCA rows, top-k 2048, latent 512, 64 heads).
 
 Prints one JSON line.  `value` = indexer scores per second of whole steps
@@ -203,6 +205,17 @@ def main():
         r = reps_for(step_s / 4)
         t_attend = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.attend(i) for i in range(r)]), r)
+        # per-step native tiered selection on the current candidates: re-score + top-k
+        r = reps_for(1e-5)
+        t_rescore = timed_graph(torch, stream, capture(
+            torch, stream, [lambda i=i: p.rescore(i) for i in range(r)]), r)
+        t_topk_native = timed_graph(torch, stream, capture(torch, stream, [p.topk_native] * r), r)
+        # OR-mode union of three indexers (three score launches, the last two combining)
+        r = max(2, reps_for(step_s) // 3)
+        t_union3 = timed_graph(torch, stream, capture(
+            torch, stream, [lambda i=i: p.score_union(3, 3 * i) for i in range(r)]), r)
+        p.score(0)
+        p.select()
 
     torch.cuda.synchronize()
     counts = p.cand_count.cpu().numpy()
@@ -216,6 +229,8 @@ def main():
     score_flops = 2.0 * scores_per_step * wl.H * wl.D
     att_alg_bytes = att_bytes + wl.qa.nbytes * 2 + wl.B * wl.k * 4   # rows, qa in, out, indices
     att_flops = 4.0 * wl.B * wl.T * wl.Hq * (wl.k + wl.max_hca) * wl.Dl
+    # native re-score: per candidate one key row, its index and its logit; the queries
+    rescore_bytes = int(counts.sum()) * (wl.D * 2 + 4 + 4) + wl.B * wl.H * (wl.D * 2 + 4)
 
     def roof(bound, alg, t, peak, unit, traffic):
         ach = alg / t / (1e9 if unit == "GB/s" else 1e12)
@@ -253,14 +268,20 @@ def main():
         "kernels_us": {"index_score": round(t_score * 1e6, 2),
                        "select_compact": round(t_select * 1e6, 2),
                        "topk": round(t_topk * 1e6, 2),
-                       "sparse_attend": round(t_attend * 1e6, 2)},
+                       "sparse_attend": round(t_attend * 1e6, 2),
+                       "index_rescore": round(t_rescore * 1e6, 2),
+                       "topk_native": round(t_topk_native * 1e6, 2),
+                       "index_score_union3": round(t_union3 * 1e6, 2)},
         "index_scores_per_s": round(scores_per_step / t_score, 1),
         "decode_tokens_per_s": round(wl.B * wl.T / t_attend, 1),
         "decode_tokens_per_s_tau64": round(
             wl.B * wl.T / (t_attend + (t_score + t_select + t_topk) / 64.0), 1),
+        "decode_tokens_per_s_native_topk": round(
+            wl.B * wl.T / (t_attend + t_rescore + t_topk_native + (t_score + t_select) / 64.0), 1),
         "selected_fraction": round(float(counts.sum()) / float(wl.seq_len.sum()), 4),
         "roofline": roofline,
         "roofline_attend": roof_att,
+        "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s", None),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -1,7 +1,7 @@
 /*
  * lsa.h -- C ABI of the Lookahead Sparse Attention (LSA) hot path on MI355X (gfx950).
  *
- * The four calls follow the decode path described on the page
+ * The calls follow the decode path described on the page
  * "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via Lookahead
  * Sparse Attention" (gist.science/paper/2606.09079), Technical Summary
  * section 2.1 "Architectural Design":
@@ -11,6 +11,8 @@
  *                          section 2.4 "Optimal Configuration";
  *   lsa_select_compact  -- keep every entry whose score reaches 0.5 ("Dynamic
  *                          Fetching"), as an ascending index list;
+ *   lsa_index_rescore   -- the native indexer's per-step score of that
+ *                          subset (rank keys for the next call);
  *   lsa_topk            -- fine-grained top-k inside that subset ("Tiered
  *                          Selection");
  *   lsa_sparse_attend   -- the final core attention over the chosen entries
@@ -85,6 +87,11 @@ extern "C" {
  *                   entry_start[b] + s -- the OR-union of the per-position
  *                   gates of section 2.4 is exactly the gate on m;
  *                   prob_out, if given, holds sigmoid(m).
+ *   reduce_max = 2: as 1, but z_out already holds the union of other
+ *                   indexers (section 2.4's OR-mode across the indexers of
+ *                   several layers: call once per indexer, the first with 1)
+ *                   and receives max(z_out, m) (a NaN on either side yields
+ *                   the other); prob_out, if given, holds its sigmoid.
  *   prob_out may be NULL.  Accumulation is fp32; bf16 products are exact.
  * Envelope: B, T, H, D >= 1; the bf16 matrix-core path takes H <= 64 and
  * D in {64, 128}; other shapes (and fp32) use the vector path, which needs
@@ -93,6 +100,32 @@ int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
                     const int32_t* seq_len, const int64_t* entry_start, int B, int T, int H,
                     int D, int64_t max_len, const void* q, const float* w, float bias,
                     int reduce_max, float* z_out, float* prob_out, void* stream);
+
+/* Native re-score of the kept subset (section 2.1 "Tiered Selection": the
+ * backbone's native Lightning Indexer takes the fine-grained top-k inside the
+ * fetched subset; section 2.3 "Decoupled Training": the compressed indexer
+ * keys are the backbone's frozen keys).  This library's reading: with its own
+ * per-step queries q' and weights w' the native indexer scores only the
+ * candidates, against the same key rows, as a ranking logit (no bias, no
+ * sigmoid):
+ *     r[b,s] = sum_h w'[b,h] * max(0, <q'[b,h,:], k[b,s,:]>)
+ * for every candidate s = cand_idx[entry_start[b] + j], j < cand_count[b]
+ * (lsa_select_compact's output layout), written at r_out[entry_start[b] + s]
+ * -- where lsa_topk reads its rank keys.  Other elements of r_out are left
+ * untouched.
+ *   keys, key_row_start: as for lsa_index_score; seq_len[b] bounds the indices
+ *              (an index outside [0, S_b) reads no key memory and writes
+ *              nothing).
+ *   q'  [B, H, D] in `dtype`; w' [B, H] fp32 (any sign).
+ *   max_cand (host) >= every cand_count[b]; it sizes the grid.
+ * Envelope: the bf16 matrix-core path takes H <= 64 and D in {64, 128} and a
+ * sequence's keys spanning < 2 GiB; other shapes (and fp32) use the vector
+ * path, which needs H*(D+1) <= 16384.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int lsa_index_rescore(const void* keys, int dtype, const int64_t* key_row_start,
+                      const int32_t* seq_len, const int64_t* entry_start,
+                      const int32_t* cand_idx, const int32_t* cand_count, int B, int H, int D,
+                      int64_t max_cand, const void* q, const float* w, float* r_out,
+                      void* stream);
 
 /* Dynamic fetching (section 2.1): keep every entry with I >= 0.5, with no
  * fixed count.  I >= 0.5 holds exactly when z >= 0, so the gate is taken on

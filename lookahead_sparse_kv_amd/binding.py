@@ -27,7 +27,8 @@ LSA_OP_SELECT = 1
 LSA_OP_TOPK = 2
 LSA_OP_ATTEND = 3
 
-EXPORTED = ["lsa_index_score", "lsa_select_compact", "lsa_topk", "lsa_sparse_attend",
+EXPORTED = ["lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+            "lsa_sparse_attend",
             "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
 
 
@@ -52,6 +53,7 @@ def load_library(path: str = LIB_PATH):
     P, I, L, F, Z = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                      ctypes.c_size_t)
     lib.lsa_index_score.argtypes = [P, I, P, P, P, I, I, I, I, L, P, P, F, I, P, P, P]
+    lib.lsa_index_rescore.argtypes = [P, I, P, P, P, P, P, I, I, I, L, P, P, P, P]
     lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
     lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, P, Z, P]
     lib.lsa_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, L, F, P, P, P, Z, P]
@@ -63,7 +65,8 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_last_error.restype = ctypes.c_char_p
     lib.lsa_version.argtypes = []
     lib.lsa_version.restype = I
-    for name in ("lsa_index_score", "lsa_select_compact", "lsa_topk", "lsa_sparse_attend"):
+    for name in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+                 "lsa_sparse_attend"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -112,8 +115,11 @@ def lsa_version() -> int:
 
 
 def lsa_index_score(keys, key_row_start, seq_len, entry_start, max_len: int, q, w, bias: float,
-                    reduce_max: bool = False, z_out=None, prob_out=None, stream=None):
-    """Score every entry (see include/lsa.h).  q: [B, T, H, D], w: [B, T, H]."""
+                    reduce_max=False, z_out=None, prob_out=None, stream=None):
+    """Score every entry (see include/lsa.h).  q: [B, T, H, D], w: [B, T, H].
+
+    reduce_max: False/0 per position, True/1 max over positions, 2 OR-union
+    with the indexers already in z_out."""
     lib = load_library()
     B, T, H, D = q.shape
     _dev(keys, "keys")
@@ -129,10 +135,32 @@ def lsa_index_score(keys, key_row_start, seq_len, entry_start, max_len: int, q, 
         _dev(prob_out, "prob_out", torch.float32)
     rc = lib.lsa_index_score(_ptr(keys), _dtype_code(keys), _ptr(key_row_start), _ptr(seq_len),
                              _ptr(entry_start), B, T, H, D, int(max_len), _ptr(q), _ptr(w),
-                             float(bias), 1 if reduce_max else 0, _ptr(z_out), _ptr(prob_out),
+                             float(bias), int(reduce_max), _ptr(z_out), _ptr(prob_out),
                              _stream(stream))
     _check("lsa_index_score", rc)
     return z_out, prob_out
+
+
+def lsa_index_rescore(keys, key_row_start, seq_len, entry_start, cand_idx, cand_count,
+                      max_cand: int, q, w, r_out, stream=None):
+    """Native re-score of each sequence's candidates (see include/lsa.h).
+    q: [B, H, D], w: [B, H]; r_out is entry-indexed fp32."""
+    lib = load_library()
+    B, H, D = q.shape
+    _dev(keys, "keys")
+    _dev(q, "q", keys.dtype)
+    _dev(w, "w", torch.float32)
+    _dev(key_row_start, "key_row_start", torch.int64)
+    _dev(seq_len, "seq_len", torch.int32)
+    _dev(entry_start, "entry_start", torch.int64)
+    _dev(cand_idx, "cand_idx", torch.int32)
+    _dev(cand_count, "cand_count", torch.int32)
+    _dev(r_out, "r_out", torch.float32)
+    rc = lib.lsa_index_rescore(_ptr(keys), _dtype_code(keys), _ptr(key_row_start), _ptr(seq_len),
+                               _ptr(entry_start), _ptr(cand_idx), _ptr(cand_count), B, H, D,
+                               int(max_cand), _ptr(q), _ptr(w), _ptr(r_out), _stream(stream))
+    _check("lsa_index_rescore", rc)
+    return r_out
 
 
 def lsa_select_compact(z, entry_start, seq_len, max_len: int, cand_idx, cand_count, workspace,

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_score_decode(
     const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int H,
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
-    float* __restrict__ z_out, float* __restrict__ prob_out) {
+    int combine, float* __restrict__ z_out, float* __restrict__ prob_out) {
     constexpr int D = 32 * KT;
     constexpr int SLOTS = D / 8;                 // 16-byte slots per key row
     constexpr int RPI = 64 / SLOTS;              // rows per direct-to-LDS instruction
@@ -160,7 +160,8 @@ __global__ __launch_bounds__(256) void k_score_decode(
         sacc += __shfl_xor(sacc, 32);
         const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
         if (g == 0 && n < last) {
-            const float z = sacc + bias;
+            float z = sacc + bias;
+            if (combine) z = fmaxf(z_out[eo + n], z);   // OR-union with earlier indexers
             z_out[eo + n] = z;
             if (prob_out) prob_out[eo + n] = sigmoidf(z);
         }
@@ -329,8 +330,10 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             if (ent[nt] < S) {
-                z_out[eo + ent[nt]] = mx[nt];
-                if (prob_out) prob_out[eo + ent[nt]] = sigmoidf(mx[nt]);
+                // reduce_max == 2: OR-union with the indexers already in z_out
+                const float m = reduce_max == 2 ? fmaxf(z_out[eo + ent[nt]], mx[nt]) : mx[nt];
+                z_out[eo + ent[nt]] = m;
+                if (prob_out) prob_out[eo + ent[nt]] = sigmoidf(m);
             }
     }
 }
@@ -375,6 +378,7 @@ __global__ __launch_bounds__(256) void k_score_vector(
         }
     }
     if (reduce_max) {
+        if (reduce_max == 2) m = fmaxf(z_out[eo + s], m);   // OR-union with earlier indexers
         z_out[eo + s] = m;
         if (prob_out) prob_out[eo + s] = sigmoidf(m);
     }
@@ -383,9 +387,10 @@ __global__ __launch_bounds__(256) void k_score_vector(
 template <int MT, int KT>
 static void launch_decode(dim3 grid, hipStream_t st, const void* keys, const int64_t* krs,
                           const int32_t* lens, const int64_t* es, int H, int64_t max_len,
-                          const void* q, const float* w, float bias, float* z, float* p) {
+                          const void* q, const float* w, float bias, int combine, float* z,
+                          float* p) {
     hipLaunchKernelGGL((k_score_decode<MT, KT>), grid, dim3(256), 0, st, (const bf16*)keys, krs,
-                       lens, es, H, max_len, (const bf16*)q, w, bias, z, p);
+                       lens, es, H, max_len, (const bf16*)q, w, bias, combine, z, p);
 }
 
 }  // namespace lsa
@@ -403,6 +408,9 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
     if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || max_len < 0)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: B=%d T=%d H=%d D=%d max_len=%lld", B, T,
                     H, D, (long long)max_len);
+    if (reduce_max < 0 || reduce_max > 2)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: reduce_max=%d not in {0, 1, 2}",
+                    reduce_max);
     if (dtype != LSA_DTYPE_F32 && dtype != LSA_DTYPE_BF16)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: unknown dtype %d", dtype);
     if (!aligned16(keys) || !aligned16(q))
@@ -431,7 +439,7 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
         const int MT = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
 #define LSA_DEC(mt, kt)                                                                      \
     launch_decode<mt, kt>(grid, st, keys, key_row_start, seq_len, entry_start, H, max_len, q, \
-                          w, bias, z_out, prob_out)
+                          w, bias, reduce_max == 2, z_out, prob_out)
         // With one position the [T, S_b] layout and the reduced layout coincide.
         if (D == 128) {
             if (MT == 1) LSA_DEC(1, 4); else if (MT == 2) LSA_DEC(2, 4); else LSA_DEC(4, 4);

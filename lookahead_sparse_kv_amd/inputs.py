@@ -296,6 +296,16 @@ def make_workload(name: str, seed: Optional[int] = None, bias: Optional[float] =
                     hca_count, float(1.0 / np.sqrt(Dl)), planted, frac)
 
 
+def native_queries(wl: Workload, seed: int = 104729):
+    """Per-step queries q' [B, H, D] and weights w' [B, H] of the backbone's native
+    indexer, drawn like the Memory Indexer's (q' ~ N(0, 1/D) in the keys' dtype,
+    w' ~ U(0, 1)); seeded from the workload's seed."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([wl.seed, seed])))
+    q = _normal(rng, (wl.B, wl.H, wl.D), 1.0 / np.sqrt(wl.D))
+    w = rng.uniform(0.0, 1.0, size=(wl.B, wl.H)).astype(np.float32)
+    return (to_bf16_bits(q) if wl.dtype == "bf16" else q), w
+
+
 def random_small(seed: int, B: int, T: int, H: int, D: int, lens, dtype: str = "bf16",
                  k: int = 16, Hq: int = 16, Dl: int = 128, hca_lens=None, bias: float = 0.0,
                  shared: bool = False, w_low: float = 0.0, int_valued: bool = False) -> Workload:

@@ -50,6 +50,10 @@ class DeviceInputs:
         self.key_row_start = _to_dev(wl.key_row_start.astype(np.int64), device)
         self.entry_start = _to_dev(wl.entry_start.astype(np.int64), device)
         self.qa = _to_dev(wl.qa, device)
+        from .inputs import native_queries
+        q2, w2 = native_queries(wl)
+        self.q_native = _to_dev(q2, device)     # the native indexer's per-step queries
+        self.w_native = _to_dev(w2, device)
         if wl.latent is not None:
             lat = _to_dev(wl.latent, device)
             self.latent = [lat] + [lat.clone() for _ in range(latent_replicas - 1)]
@@ -90,12 +94,35 @@ class Pipeline:
         ws_a = lsa.lsa_workspace_bytes(lsa.LSA_OP_ATTEND, B, T, d.Hq, d.Dl, k=d.k,
                                        max_hca=d.max_hca)
         self.ws_attend = torch.empty(max(1, ws_a), dtype=torch.uint8, device=dev)
+        self.r = torch.zeros(n, dtype=torch.float32, device=dev)   # native re-score (entry-indexed)
 
     def score(self, replica: int = 0, stream=None):
         d = self.d
         lsa.lsa_index_score(d.keys[replica % len(d.keys)], d.key_row_start, d.seq_len,
                             d.entry_start, d.max_len, d.q, d.w, d.bias, reduce_max=True,
                             z_out=self.z, prob_out=self.prob, stream=stream)
+
+    def score_union(self, n_indexers: int, replica: int = 0, stream=None):
+        """OR-mode union of n indexers (key replicas replica .. replica+n-1 stand in
+        for the indexers' key sets), gate logits left in z."""
+        d = self.d
+        for i in range(n_indexers):
+            lsa.lsa_index_score(d.keys[(replica + i) % len(d.keys)], d.key_row_start, d.seq_len,
+                                d.entry_start, d.max_len, d.q, d.w, d.bias,
+                                reduce_max=1 if i == 0 else 2, z_out=self.z, stream=stream)
+
+    def rescore(self, replica: int = 0, stream=None):
+        """The native indexer's per-step score of the kept entries, into r."""
+        d = self.d
+        lsa.lsa_index_rescore(d.keys[replica % len(d.keys)], d.key_row_start, d.seq_len,
+                              d.entry_start, self.cand_idx, self.cand_count, d.max_len,
+                              d.q_native, d.w_native, self.r, stream=stream)
+
+    def topk_native(self, stream=None):
+        """Top-k of the kept entries by the native re-score."""
+        d = self.d
+        lsa.lsa_topk(self.r, d.entry_start, d.seq_len, d.max_len, self.cand_idx, self.cand_count,
+                     d.k, self.topk_idx, self.topk_count, self.ws_topk, stream=stream)
 
     def select(self, stream=None):
         d = self.d

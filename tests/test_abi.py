@@ -29,10 +29,11 @@ def lib():
     return binding.load_library()
 
 
-def test_header_declares_the_four_calls():
+def test_header_declares_the_calls():
     syms = declared_symbols()
-    for s in ("lsa_index_score", "lsa_select_compact", "lsa_topk", "lsa_sparse_attend",
-              "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"):
+    for s in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+              "lsa_sparse_attend", "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error",
+              "lsa_version"):
         assert s in syms
     assert sorted(binding.EXPORTED) == syms
 
@@ -130,3 +131,34 @@ def test_workspace_sizes(lib):
     assert lib.lsa_workspace_bytes(2, 8, 0, 0, 0, 32769, 2048, 0) == 8 * 32769 * 4
     # one (b, t) pair per CU-sized split plan: B*T large -> no split, no workspace
     assert lib.lsa_workspace_bytes(3, 16, 64, 64, 512, 0, 2048, 0) == 0
+
+
+def test_score_reduce_mode_validation(lib):
+    P = FAKE
+    f = lib.lsa_index_score
+    base = [P, 1, P, P, P, 2, 1, 64, 128, 1000, P, P, 0.0, 1, P, None, None]
+    for mode in (-1, 3):
+        a = list(base); a[13] = mode
+        assert f(*a) == -1
+        assert b"reduce_max" in lib.lsa_last_error()
+
+
+def test_rescore_validation(lib):
+    P = FAKE
+    f = lib.lsa_index_rescore
+    args = [P, 1, P, P, P, P, P, 8, 64, 128, 20000, P, P, P, None]
+    for i in (0, 2, 3, 4, 5, 6, 11, 12, 13):          # every required pointer
+        a = list(args); a[i] = None
+        assert f(*a) == -1, i
+    a = list(args); a[7] = 0                        # B = 0
+    assert f(*a) == -1
+    a = list(args); a[10] = -1                      # max_cand < 0
+    assert f(*a) == -1
+    a = list(args); a[1] = 7                        # dtype
+    assert f(*a) == -1
+    a = list(args); a[0] = MISALIGNED
+    assert f(*a) == -1
+    a = list(args); a[7] = 70000                    # B too large
+    assert f(*a) == -2
+    a = list(args); a[1] = 0; a[8] = 200; a[9] = 200  # fp32 vector path too large
+    assert f(*a) == -2
