@@ -161,6 +161,8 @@ def main():
         if args.profile_launches:
             for i in range(args.profile_launches):
                 p.step(i)
+            for i in range(args.profile_launches):
+                p.rescore(i)
             if args.copy_bytes:
                 a = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
                 b = torch.empty_like(a)

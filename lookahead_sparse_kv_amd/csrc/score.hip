@@ -58,12 +58,12 @@ __device__ __forceinline__ void wait_vmcnt_score() {
 //   each 32 dims; A (queries) stays in registers for the whole wave; B (keys)
 //   for k-step kk is dims 32kk + 8g .. +7 of entry n.
 //   D[4g+v][n] of head tile mt is head 16mt + 4g + v of entry n.
-template <int MT, int KT>
+template <int MT, int KT, bool COMBINE>
 __global__ __launch_bounds__(256) void k_score_decode(
     const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int H,
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
-    int combine, float* __restrict__ z_out, float* __restrict__ prob_out) {
+    float* __restrict__ z_out, float* __restrict__ prob_out) {
     constexpr int D = 32 * KT;
     constexpr int SLOTS = D / 8;                 // 16-byte slots per key row
     constexpr int RPI = 64 / SLOTS;              // rows per direct-to-LDS instruction
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k_score_decode(
         const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
         if (g == 0 && n < last) {
             float z = sacc + bias;
-            if (combine) z = fmaxf(z_out[eo + n], z);   // OR-union with earlier indexers
+            if (COMBINE) z = fmaxf(z_out[eo + n], z);   // OR-union with earlier indexers
             z_out[eo + n] = z;
             if (prob_out) prob_out[eo + n] = sigmoidf(z);
         }
@@ -387,10 +387,17 @@ __global__ __launch_bounds__(256) void k_score_vector(
 template <int MT, int KT>
 static void launch_decode(dim3 grid, hipStream_t st, const void* keys, const int64_t* krs,
                           const int32_t* lens, const int64_t* es, int H, int64_t max_len,
-                          const void* q, const float* w, float bias, int combine, float* z,
+                          const void* q, const float* w, float bias, bool combine, float* z,
                           float* p) {
-    hipLaunchKernelGGL((k_score_decode<MT, KT>), grid, dim3(256), 0, st, (const bf16*)keys, krs,
-                       lens, es, H, max_len, (const bf16*)q, w, bias, combine, z, p);
+    // the OR-union mode is its own instantiation: the plain kernel keeps its code
+    if (combine)
+        hipLaunchKernelGGL((k_score_decode<MT, KT, true>), grid, dim3(256), 0, st,
+                           (const bf16*)keys, krs, lens, es, H, max_len, (const bf16*)q, w, bias, z,
+                           p);
+    else
+        hipLaunchKernelGGL((k_score_decode<MT, KT, false>), grid, dim3(256), 0, st,
+                           (const bf16*)keys, krs, lens, es, H, max_len, (const bf16*)q, w, bias, z,
+                           p);
 }
 
 }  // namespace lsa
