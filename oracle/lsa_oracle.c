@@ -124,6 +124,7 @@ int lsa_ref_select(const double* z, const int64_t* entry_start, const int32_t* s
 typedef struct {
     double r;
     int32_t s;
+    int32_t j;    /* position in the candidate list */
 } ranked_t;
 
 /* Order: larger r first; NaN after every number; equal r -> smaller s first. */
@@ -144,7 +145,7 @@ static int by_index(const void* pa, const void* pb) {
 /* O3 -- TS 2.1 "Tiered Selection". */
 int lsa_ref_topk(const double* r, const int64_t* entry_start, const int32_t* seq_len,
                  int B, const int32_t* cand_idx, const int32_t* cand_count, int k,
-                 int32_t* topk_idx, int32_t* topk_count) {
+                 int out_positions, int32_t* topk_idx, int32_t* topk_count) {
     if (!r || !entry_start || !seq_len || !cand_idx || !cand_count || !topk_idx || !topk_count)
         return -1;
     if (B <= 0 || k <= 0) return -1;
@@ -156,12 +157,13 @@ int lsa_ref_topk(const double* r, const int64_t* entry_start, const int32_t* seq
         for (int32_t j = 0; j < n; ++j) {
             const int32_t s = cand_idx[entry_start[b] + j];
             items[j].s = s;
+            items[j].j = j;
             items[j].r = r[entry_start[b] + s];
         }
         qsort(items, (size_t)n, sizeof(ranked_t), by_rank);
         const int32_t keep = n < k ? n : k;
         int32_t* out = topk_idx + (int64_t)b * k;
-        for (int32_t j = 0; j < keep; ++j) out[j] = items[j].s;
+        for (int32_t j = 0; j < keep; ++j) out[j] = out_positions ? items[j].j : items[j].s;
         qsort(out, (size_t)keep, sizeof(int32_t), by_index);
         topk_count[b] = keep;
         free(items);
@@ -228,6 +230,23 @@ int lsa_ref_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int D
         free(row_off);
         free(row_src);
         free(logit);
+    }
+    return 0;
+}
+
+/* O5 -- TS 2.1 "Dynamic Fetching": the kept rows, copied in list order. */
+int lsa_ref_fetch_rows(const void* src, int64_t row_bytes, const int64_t* src_row_start,
+                       const int32_t* idx, const int64_t* idx_start, const int32_t* count,
+                       int B, void* dst, const int64_t* dst_row_start) {
+    if (!src || !src_row_start || !idx || !idx_start || !count || !dst || !dst_row_start) return -1;
+    if (B <= 0 || row_bytes <= 0) return -1;
+    for (int b = 0; b < B; ++b) {
+        for (int32_t j = 0; j < count[b]; ++j) {
+            const int64_t from = src_row_start[b] + idx[idx_start[b] + j];
+            const int64_t to = dst_row_start[b] + j;
+            memcpy((char*)dst + to * row_bytes, (const char*)src + from * row_bytes,
+                   (size_t)row_bytes);
+        }
     }
     return 0;
 }

@@ -78,10 +78,20 @@ int lsa_ref_select(const double* z, const int64_t* entry_start, const int32_t* s
  * inside the kept subset).  Candidates of sequence b are ordered by rank key
  * r[entry_start[b]+s] descending, equal keys by smaller s first, NaN last;
  * the first min(k, count) are kept and written in ascending s to
- * topk_idx[b*k ...]; topk_count[b] = min(k, count). */
+ * topk_idx[b*k ...]; topk_count[b] = min(k, count).  With out_positions != 0
+ * the row holds instead each kept entry's position j in the candidate list
+ * (cand_idx[entry_start[b]+j] = s), ascending. */
 int lsa_ref_topk(const double* r, const int64_t* entry_start, const int32_t* seq_len,
                  int B, const int32_t* cand_idx, const int32_t* cand_count, int k,
-                 int32_t* topk_idx, int32_t* topk_count);
+                 int out_positions, int32_t* topk_idx, int32_t* topk_count);
+
+/* O5  Just-in-time fetch (TS 2.1 "Dynamic Fetching": the kept entries are
+ * fetched from the CPU-side cold pool into GPU memory).  Row copy:
+ *   dst row dst_row_start[b]+j = src row src_row_start[b] + idx[idx_start[b]+j]
+ * for j < count[b]; rows are row_bytes long; other dst rows are untouched. */
+int lsa_ref_fetch_rows(const void* src, int64_t row_bytes, const int64_t* src_row_start,
+                       const int32_t* idx, const int64_t* idx_start, const int32_t* count,
+                       int B, void* dst, const int64_t* dst_row_start);
 
 /* O4  Core attention over the chosen entries (TS 2.1 "Tiered Selection",
  * final core attention) together with every heavily compressed (HCA) entry,

@@ -44,11 +44,12 @@ def _bind(path):
     D = ctypes.c_double
     lib.lsa_ref_index_score.argtypes = [P, I, P, P, P, I, I, I, I, P, P, D, I, P, P]
     lib.lsa_ref_select.argtypes = [P, P, P, I, D, P, P]
-    lib.lsa_ref_topk.argtypes = [P, P, P, I, P, P, I, P, P]
+    lib.lsa_ref_topk.argtypes = [P, P, P, I, P, P, I, I, P, P]
+    lib.lsa_ref_fetch_rows.argtypes = [P, ctypes.c_int64, P, P, P, P, I, P, P]
     lib.lsa_ref_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, D, P, P]
     lib.lsa_ref_index_rescore.argtypes = [P, I, P, P, P, P, I, I, I, P, P, P]
     for f in (lib.lsa_ref_index_score, lib.lsa_ref_select, lib.lsa_ref_topk,
-              lib.lsa_ref_sparse_attend, lib.lsa_ref_index_rescore):
+              lib.lsa_ref_sparse_attend, lib.lsa_ref_index_rescore, lib.lsa_ref_fetch_rows):
         f.restype = ctypes.c_int
     return lib
 
@@ -190,8 +191,9 @@ def select(z, entry_start, seq_len, threshold=0.0):
     return cand_idx, cand_count
 
 
-def topk(r, entry_start, seq_len, cand_idx, cand_count, k):
-    """O3: top-k (rank key descending, ties to the smaller index), ascending."""
+def topk(r, entry_start, seq_len, cand_idx, cand_count, k, positions=False):
+    """O3: top-k (rank key descending, ties to the smaller index), ascending; entry
+    indices, or with positions the positions in the candidate list."""
     lib = _load()
     r = _c(r, np.float64)
     entry_start = _c(entry_start, np.int64)
@@ -199,12 +201,16 @@ def topk(r, entry_start, seq_len, cand_idx, cand_count, k):
     cand_idx = _c(cand_idx, np.int32)
     cand_count = _c(cand_count, np.int32)
     B = len(seq_len)
-    topk_idx = np.full(B * k, -1, dtype=np.int32)
+    guard = 64                     # a write past B*k entries lands here and is reported
+    buf = np.full(B * k + guard, -1, dtype=np.int32)
     topk_count = np.zeros(B, dtype=np.int32)
     rc = lib.lsa_ref_topk(_ptr(r), _ptr(entry_start), _ptr(seq_len), B, _ptr(cand_idx),
-                          _ptr(cand_count), int(k), _ptr(topk_idx), _ptr(topk_count))
+                          _ptr(cand_count), int(k), 1 if positions else 0, _ptr(buf),
+                          _ptr(topk_count))
     _check(rc, "topk")
-    return topk_idx.reshape(B, k), topk_count
+    if np.any(buf[B * k:] != -1):
+        raise ValueError("topk wrote past its B*k outputs")
+    return buf[:B * k].reshape(B, k), topk_count
 
 
 def sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k, hca=None,
@@ -235,6 +241,25 @@ def sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k, hca=Non
                                    float(scale), _ptr(out), _ptr(lse))
     _check(rc, "sparse_attend")
     return out, lse
+
+
+def fetch_rows(src, src_row_start, idx, idx_start, count, dst_rows, dst_row_start, dst_init=None):
+    """O5: rows src[src_row_start[b] + idx[idx_start[b] + j]] copied to
+    dst[dst_row_start[b] + j]; dst has dst_rows rows (dst_init, else zeros)."""
+    lib = _load()
+    src = np.ascontiguousarray(src)
+    row_shape = src.shape[1:]
+    dst = (np.zeros((dst_rows,) + row_shape, src.dtype) if dst_init is None
+           else np.array(dst_init, dtype=src.dtype, copy=True))
+    assert dst.shape == (dst_rows,) + row_shape
+    row_bytes = int(src.itemsize * int(np.prod(row_shape)))
+    count = _c(count, np.int32)
+    rc = lib.lsa_ref_fetch_rows(_ptr(src), row_bytes, _ptr(_c(src_row_start, np.int64)),
+                                _ptr(_c(idx, np.int32)), _ptr(_c(idx_start, np.int64)),
+                                _ptr(count), len(count), _ptr(dst),
+                                _ptr(_c(dst_row_start, np.int64)))
+    _check(rc, "fetch_rows")
+    return dst
 
 
 def bf16_bits_to_f64(bits):

@@ -40,6 +40,14 @@ MUTANTS = {
     "union_drops_previous": ("if (reduce_max == 2 && (isnan(m) || prev > m)) m = prev;", ""),
     "union_takes_min": ("if (reduce_max == 2 && (isnan(m) || prev > m)) m = prev;",
                         "if (reduce_max == 2 && (isnan(m) || prev < m)) m = prev;"),
+    "positions_are_entries": ("out[j] = out_positions ? items[j].j : items[j].s;",
+                              "out[j] = items[j].s;"),
+    "fetch_dst_offset_dropped": ("const int64_t to = dst_row_start[b] + j;",
+                                 "const int64_t to = j;"),
+    "fetch_src_offset_dropped": ("const int64_t from = src_row_start[b] + idx[idx_start[b] + j];",
+                                 "const int64_t from = idx[idx_start[b] + j];"),
+    "fetch_list_offset_dropped": ("const int64_t from = src_row_start[b] + idx[idx_start[b] + j];",
+                                  "const int64_t from = src_row_start[b] + idx[j];"),
 }
 
 

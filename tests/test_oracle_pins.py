@@ -455,3 +455,69 @@ def test_union_over_indexers(ref, seed):
         for z in zs:
             gate_or |= z[es[b]:es[b] + lens[b]] >= 0.0
         assert cu[es[b]:es[b] + cnu[b]].tolist() == np.flatnonzero(gate_or).tolist()
+
+
+# ----------------------------------------------- just-in-time fetch (O5) and positions
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_positions_brute_force(ref, seed):
+    """Positions mode: each kept entry's place in the candidate list, i.e. the
+    brute-force kept set looked up in the list."""
+    rng = np.random.default_rng(300 + seed)
+    S = int(rng.integers(1, 16))
+    r = rng.integers(-2, 3, size=S).astype(np.float64)
+    cands = sorted(rng.choice(S, size=int(rng.integers(0, S + 1)), replace=False).tolist())
+    k = int(rng.integers(1, S + 2))
+    cand_idx = np.full(S, -1, np.int32)
+    cand_idx[:len(cands)] = cands
+    args = (r, np.zeros(1, np.int64), np.array([S], np.int32), cand_idx,
+            np.array([len(cands)], np.int32), k)
+    t, tc = ref.topk(*args, positions=True)
+    assert t[0, :tc[0]].tolist() == [cands.index(c) for c in _brute_topk(r, cands, k)]
+
+
+def test_fetch_rows_is_a_gather(ref):
+    """Fetched row j of sequence b is row src_row_start[b] + idx[idx_start[b] + j]
+    of the pool (numpy fancy indexing); rows past the count stay as they were."""
+    rng = np.random.default_rng(21)
+    pool = rng.integers(0, 1 << 16, size=(200, 40), dtype=np.uint16)
+    srs = np.array([0, 120, 60], np.int64)
+    idx = np.array([5, 9, 0, 11, 3, 2, 79, 1, 0], np.int32)
+    ist = np.array([0, 4, 4], np.int64)
+    cnt = np.array([4, 0, 5], np.int32)
+    drs = np.array([10, 0, 20], np.int64)
+    init = rng.integers(0, 1 << 16, size=(30, 40), dtype=np.uint16)
+    out = ref.fetch_rows(pool, srs, idx, ist, cnt, 30, drs, dst_init=init)
+    want = init.copy()
+    want[10:14] = pool[0 + idx[0:4]]
+    want[20:25] = pool[60 + idx[4:9]]
+    assert np.array_equal(out, want)
+    # identity list: the fetch is the pool's prefix
+    ident = ref.fetch_rows(pool, np.zeros(1, np.int64), np.arange(200, dtype=np.int32),
+                           np.zeros(1, np.int64), np.array([200], np.int32), 200,
+                           np.zeros(1, np.int64))
+    assert np.array_equal(ident, pool)
+
+
+def test_attention_over_fetched_rows_equals_attention_over_pool(ref):
+    """Fetch the top-k rows into a hot buffer and address them by position: the
+    attention output equals attention over the pool addressed by entry index."""
+    rng = np.random.default_rng(22)
+    lens = np.array([90, 33], np.int32)
+    es = np.array([0, 90], np.int64)
+    B, T, Hq, Dl, k = 2, 2, 3, 16, 8
+    z = rng.standard_normal(int(lens.sum()))
+    cand, cnt = ref.select(z, es, lens)
+    t, tc = ref.topk(z, es, lens, cand, cnt, k)
+    pos, pc = ref.topk(z, es, lens, cand, cnt, k, positions=True)
+    assert np.array_equal(tc, pc)
+    for b in range(B):
+        assert np.array_equal(cand[es[b] + pos[b, :pc[b]]], t[b, :tc[b]])
+    pool = rng.standard_normal((int(lens.sum()), Dl)).astype(np.float32)
+    # the hot buffer holds every candidate of each sequence, in list order
+    hot_rs = np.array([0, int(cnt[0])], np.int64)
+    hot = ref.fetch_rows(pool, es, cand, es, cnt, int(cnt.sum()), hot_rs)
+    qa = rng.standard_normal((B, T, Hq, Dl)).astype(np.float32)
+    o1, l1 = ref.sparse_attend(qa, pool, es, t, tc, k, scale=0.2)
+    o2, l2 = ref.sparse_attend(qa, hot, hot_rs, pos, pc, k, scale=0.2)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
