@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences the CPU baseline scores")
     ap.add_argument("--kernel-reps", type=int, default=0,
                     help="launches per timing interval (0 = pick for >= 1 ms)")
+    ap.add_argument("--fetch-reps", type=int, default=4,
+                    help="back-to-back fetches per timed interval")
     ap.add_argument("--profile-launches", type=int, default=0,
                     help="only run N launches of each kernel (for rocprofv3 counter runs)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -83,6 +85,24 @@ def capture(torch, stream, fns):
         for f in fns:
             f()
     return g
+
+
+def timed_eager(torch, stream, calls, launches, intervals=5, warm=1):
+    """Median seconds per launch of `calls` (`launches` launches) issued eagerly on
+    `stream`, for long launches whose issue cost is small beside their run time."""
+    res = []
+    with torch.cuda.stream(stream):
+        for it in range(warm + intervals):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for c in calls:
+                c()
+            e1.record(stream)
+            e1.synchronize()
+            if it >= warm:
+                res.append(e0.elapsed_time(e1) * 1e-3 / launches)
+    return statistics.median(res)
 
 
 def timed_graph(torch, stream, g, launches, intervals=7, warm=2):
@@ -218,6 +238,23 @@ def main():
             torch, stream, [lambda i=i: p.score_union(3, 3 * i) for i in range(r)]), r)
         p.score(0)
         p.select()
+        # just-in-time fetch of the kept latent rows into a hot buffer, once per
+        # lookahead trigger: from a pinned host cold pool, and from device memory
+        fetch = None
+        if d.latent[0] is not None:
+            pool = torch.empty(d.latent[0].shape, dtype=d.latent[0].dtype, pin_memory=True)
+            pool.copy_(d.latent[0])
+            hot = torch.empty_like(d.latent[0])
+            torch.cuda.synchronize()
+            fr = args.fetch_reps
+            t_fetch_host = timed_eager(torch, stream, [lambda: p.fetch(pool, hot)] * fr, fr)
+            nl = len(d.latent)
+            t_fetch_dev = timed_eager(torch, stream, [lambda i=i: p.fetch(d.latent[i % nl], hot)
+                                                      for i in range(fr)], fr)
+            # the DMA engines' own rate for a plain pinned-host -> device copy of the pool
+            t_h2d = timed_eager(torch, stream, [lambda: hot.copy_(pool, non_blocking=True)], 1)
+            fetch = (t_fetch_host, t_fetch_dev, t_h2d, pool.numel() * pool.element_size())
+            del pool, hot
 
     torch.cuda.synchronize()
     counts = p.cand_count.cpu().numpy()
@@ -286,6 +323,18 @@ def main():
         "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s", None),
         "cpu_baseline": None,
     }
+    if fetch is not None:
+        t_fh, t_fd, t_h2d, pool_bytes = fetch
+        fetched = int(counts.sum()) * wl.Dl * 2
+        line["kernels_us"]["fetch_rows_pinned_host"] = round(t_fh * 1e6, 2)
+        line["kernels_us"]["fetch_rows_device"] = round(t_fd * 1e6, 2)
+        line["fetch"] = {
+            "rows": int(counts.sum()), "bytes": fetched,
+            "pinned_host_GBs": round(fetched / t_fh / 1e9, 2),
+            "device_GBs": round(2 * fetched / t_fd / 1e9, 1),   # read + write
+            "h2d_dma_copy_GBs": round(pool_bytes / t_h2d / 1e9, 2),
+            "per_step_us_tau64": round(t_fh * 1e6 / 64.0, 2),
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seqs)
     print(json.dumps(line))

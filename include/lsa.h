@@ -13,6 +13,8 @@
  *                          Fetching"), as an ascending index list;
  *   lsa_index_rescore   -- the native indexer's per-step score of that
  *                          subset (rank keys for the next call);
+ *   lsa_fetch_rows      -- copy the kept entries' rows from the cold pool
+ *                          into a hot buffer ("Dynamic Fetching");
  *   lsa_topk            -- fine-grained top-k inside that subset ("Tiered
  *                          Selection");
  *   lsa_sparse_attend   -- the final core attention over the chosen entries
@@ -148,14 +150,41 @@ int lsa_select_compact(const float* z, const int64_t* entry_start, const int32_t
  * s, NaN after every number, -0.0 equal to +0.0.
  *   cand_idx/cand_count as written by lsa_select_compact (cand_count[b] <= S_b).
  *   topk_idx   int32 [B, k]: the kept s of sequence b in ascending order in
- *              row b; entries past topk_count[b] are left untouched.
+ *              row b; entries past topk_count[b] are left untouched.  With
+ *              out_positions != 0 the row holds instead the kept entries'
+ *              positions j in the candidate list (cand_idx[entry_start[b]+j]
+ *              = s), also ascending: the rows of a hot buffer filled by
+ *              lsa_fetch_rows from that list.
  *   topk_count int32 [B] = min(k, cand_count[b]).
  *   workspace  lsa_workspace_bytes(LSA_OP_TOPK, B, 0, 0, 0, max_len, k, 0) bytes.
  * Envelope: 1 <= k <= 65536.  Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 int lsa_topk(const float* rank_key, const int64_t* entry_start, const int32_t* seq_len, int B,
              int64_t max_len, const int32_t* cand_idx, const int32_t* cand_count, int k,
-             int32_t* topk_idx, int32_t* topk_count, void* workspace, size_t workspace_bytes,
-             void* stream);
+             int32_t* topk_idx, int32_t* topk_count, int out_positions, void* workspace,
+             size_t workspace_bytes, void* stream);
+
+/* Just-in-time fetch of the kept entries (section 2.1 "Dynamic Fetching":
+ * the entries whose score reaches 0.5 are fetched from the CPU-side cold pool
+ * into GPU memory, which holds only this critical subset).  Row copy:
+ *     dst row dst_row_start[b] + j  <-  src row src_row_start[b] + idx[idx_start[b] + j]
+ * for j < count[b], each row row_bytes long.  With idx = cand_idx, idx_start =
+ * entry_start and count = cand_count (lsa_select_compact's output), dst holds
+ * sequence b's kept rows in list order; lsa_topk(..., out_positions = 1)
+ * then names rows of dst, and lsa_sparse_attend can attend over dst with
+ * latent_row_start = dst_row_start.
+ *   src        host memory that is pinned and mapped into the device's
+ *              address space (hipHostMalloc / a pinned torch tensor), or
+ *              device memory; read by the GPU directly (zero copy).
+ *              Pageable host memory is refused (INVALID_ARG).
+ *   dst        device memory, rows of row_bytes; the caller sizes each
+ *              sequence's rows for its largest count.
+ *   row_bytes  a positive multiple of 16; src and dst 16-byte aligned.
+ *   max_count (host) >= every count[b]; it sizes the grid.  idx values must
+ *              be valid rows of sequence b's source range (not checked).
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int lsa_fetch_rows(const void* src, int64_t row_bytes, const int64_t* src_row_start,
+                   const int32_t* idx, const int64_t* idx_start, const int32_t* count, int B,
+                   int64_t max_count, void* dst, const int64_t* dst_row_start, void* stream);
 
 /* Core attention over the chosen entries plus all HCA entries (section 2.1).
  * One latent row per compressed entry serves as both key and value for all

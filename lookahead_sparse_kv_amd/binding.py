@@ -28,6 +28,7 @@ LSA_OP_TOPK = 2
 LSA_OP_ATTEND = 3
 
 EXPORTED = ["lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+            "lsa_fetch_rows",
             "lsa_sparse_attend",
             "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
 
@@ -55,7 +56,8 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_index_score.argtypes = [P, I, P, P, P, I, I, I, I, L, P, P, F, I, P, P, P]
     lib.lsa_index_rescore.argtypes = [P, I, P, P, P, P, P, I, I, I, L, P, P, P, P]
     lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
-    lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, P, Z, P]
+    lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, I, P, Z, P]
+    lib.lsa_fetch_rows.argtypes = [P, L, P, P, P, P, I, L, P, P, P]
     lib.lsa_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, L, F, P, P, P, Z, P]
     lib.lsa_workspace_bytes.argtypes = [I, I, I, I, I, L, I, L]
     lib.lsa_workspace_bytes.restype = Z
@@ -66,6 +68,7 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_version.argtypes = []
     lib.lsa_version.restype = I
     for name in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+                 "lsa_fetch_rows",
                  "lsa_sparse_attend"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -179,7 +182,9 @@ def lsa_select_compact(z, entry_start, seq_len, max_len: int, cand_idx, cand_cou
 
 
 def lsa_topk(rank_key, entry_start, seq_len, max_len: int, cand_idx, cand_count, k: int,
-             topk_idx, topk_count, workspace=None, stream=None):
+             topk_idx, topk_count, workspace=None, stream=None, out_positions: bool = False):
+    """Top-k of each candidate list (see include/lsa.h); entry indices, or with
+    out_positions the positions in the candidate list."""
     lib = load_library()
     _dev(rank_key, "rank_key", torch.float32)
     _dev(topk_idx, "topk_idx", torch.int32)
@@ -188,9 +193,35 @@ def lsa_topk(rank_key, entry_start, seq_len, max_len: int, cand_idx, cand_count,
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib.lsa_topk(_ptr(rank_key), _ptr(entry_start), _ptr(seq_len), B, int(max_len),
                       _ptr(cand_idx), _ptr(cand_count), int(k), _ptr(topk_idx), _ptr(topk_count),
-                      _ptr(workspace), ws_bytes, _stream(stream))
+                      1 if out_positions else 0, _ptr(workspace), ws_bytes, _stream(stream))
     _check("lsa_topk", rc)
     return topk_idx, topk_count
+
+
+def lsa_fetch_rows(src, src_row_start, idx, idx_start, count, max_count: int, dst, dst_row_start,
+                   stream=None):
+    """Copy rows src[src_row_start[b] + idx[idx_start[b] + j]] to dst[dst_row_start[b] + j]
+    (see include/lsa.h).  src: a pinned host tensor or a device tensor; dst: device."""
+    lib = load_library()
+    if not (src.is_cuda or src.is_pinned()):
+        raise ValueError("src must be a device tensor or pinned host memory")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    _dev(dst, "dst", src.dtype)
+    for t, n in ((src_row_start, "src_row_start"), (idx_start, "idx_start"),
+                 (dst_row_start, "dst_row_start")):
+        _dev(t, n, torch.int64)
+    _dev(idx, "idx", torch.int32)
+    _dev(count, "count", torch.int32)
+    row_bytes = src.shape[-1] * src.element_size()
+    if dst.shape[-1] * dst.element_size() != row_bytes:
+        raise ValueError("src and dst rows differ in size")
+    B = count.numel()
+    rc = lib.lsa_fetch_rows(_ptr(src), int(row_bytes), _ptr(src_row_start), _ptr(idx),
+                            _ptr(idx_start), _ptr(count), B, int(max_count), _ptr(dst),
+                            _ptr(dst_row_start), _stream(stream))
+    _check("lsa_fetch_rows", rc)
+    return dst
 
 
 def lsa_sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k: int, out,

@@ -4,7 +4,9 @@
 // Lookahead Sparse Attention", Technical Summary 2.1 "Tiered Selection": once
 // the critical subset is resident, a top-k inside it picks the entries for the
 // core attention.  Ranking: larger key first, equal keys by smaller entry
-// index, NaN last, -0.0 == +0.0.  The kept set is returned in ascending index.
+// index, NaN last, -0.0 == +0.0.  The kept set is returned in ascending index,
+// as entry indices or (out_positions) as positions in the candidate list -- the
+// rows of a hot buffer that holds the candidates' rows in list order.
 //
 // One workgroup (1024 threads) per sequence.  Keys are mapped to
 // order-preserving uint32.  The k-th largest key U is found digit by digit,
@@ -157,7 +159,7 @@ __device__ __forceinline__ void rank_list(const uint32_t* list, int m, int need,
 // RC >= cpw is the register window: every per-chunk loop is unrolled RC times
 // and the code runs once per workgroup, so the caller picks the smallest RC
 // that fits (instruction fetch of unused chunk bodies costs real time).
-template <int RC>
+template <int RC, bool POS>
 __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restrict__ cand, int n,
                           int k, int32_t* __restrict__ out, unsigned* hist, uint32_t* shortl,
                           int* scratch, int* sh) {
@@ -324,7 +326,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
             const uint64_t be = __ballot(e);
             const bool sel = g || (e && eqs + lanes_below(be) < need);
             const uint64_t bs = __ballot(sel);
-            if (sel) out[pos + lanes_below(bs)] = cr[u];
+            if (sel) out[pos + lanes_below(bs)] = POS ? wb + kWave * u + lane : cr[u];
             pos += __popcll(bs);
             eqs += __popcll(be);
         }
@@ -391,7 +393,7 @@ __device__ void radix_refine(const uint32_t* keys, int n, RadixState& st, unsign
 }
 
 // n > kRegCap: keys in the global scratch area (plain layout).
-template <bool IN_LDS>
+template <bool IN_LDS, bool POS>
 __device__ void topk_global(const float* __restrict__ rb, const int32_t* __restrict__ cand, int n,
                             int k, uint32_t* keys, int32_t* __restrict__ out, unsigned* hist,
                             uint32_t* shortl, int* scratch, int* sh) {
@@ -462,9 +464,9 @@ __device__ void topk_global(const float* __restrict__ rb, const int32_t* __restr
     auto emit = [&](int j, int cj) {
         const uint32_t key = keys[P(j)];
         if (key > U) {
-            out[pos++] = cj;
+            out[pos++] = POS ? j : cj;
         } else if (key == U) {
-            if (eq_seen < need) out[pos++] = cj;
+            if (eq_seen < need) out[pos++] = POS ? j : cj;
             ++eq_seen;
         }
     };
@@ -481,6 +483,7 @@ __device__ void topk_global(const float* __restrict__ rb, const int32_t* __restr
     }
 }
 
+template <bool POS>
 __global__ __launch_bounds__(kTkThreads) void k_topk(
     const float* __restrict__ r, const int64_t* __restrict__ entry_start,
     const int32_t* __restrict__ seq_len, int64_t max_len, const int32_t* __restrict__ cand_idx,
@@ -497,13 +500,13 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
     const int32_t* cand = cand_idx + eo;
     int32_t* out = topk_idx + (int64_t)b * k;
     if (n <= k) {
-        for (int j = threadIdx.x; j < n; j += kTkThreads) out[j] = cand[j];
+        for (int j = threadIdx.x; j < n; j += kTkThreads) out[j] = POS ? j : cand[j];
         if (threadIdx.x == 0) topk_count[b] = n;
         return;
     }
     const int cpw = (n + kTkWaves * kWave - 1) / (kTkWaves * kWave);   // chunks per wave
 #define LSA_TK_REGS(rc)                                                        \
-    else if (cpw <= rc) topk_regs<rc>(r + eo, cand, n, k, out, hist, shortl, scratch, sh);
+    else if (cpw <= rc) topk_regs<rc, POS>(r + eo, cand, n, k, out, hist, shortl, scratch, sh);
     if (false) {
     }
     // steps of 8 chunks: finer steps make workgroups of one launch run different
@@ -511,8 +514,8 @@ __global__ __launch_bounds__(kTkThreads) void k_topk(
     LSA_TK_REGS(8) LSA_TK_REGS(16) LSA_TK_REGS(24) LSA_TK_REGS(kRunChunks)
 #undef LSA_TK_REGS
     else
-        topk_global<false>(r + eo, cand, n, k, gkeys + (int64_t)b * max_len, out, hist, shortl,
-                           scratch, sh);
+        topk_global<false, POS>(r + eo, cand, n, k, gkeys + (int64_t)b * max_len, out, hist,
+                                shortl, scratch, sh);
     if (threadIdx.x == 0) topk_count[b] = k;
 }
 
@@ -526,8 +529,8 @@ size_t lsa_topk_workspace(int B, int64_t max_len) {
 
 extern "C" int lsa_topk(const float* rank_key, const int64_t* entry_start, const int32_t* seq_len,
                         int B, int64_t max_len, const int32_t* cand_idx, const int32_t* cand_count,
-                        int k, int32_t* topk_idx, int32_t* topk_count, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        int k, int32_t* topk_idx, int32_t* topk_count, int out_positions,
+                        void* workspace, size_t workspace_bytes, void* stream) {
     clear_error();
     if (!rank_key || !entry_start || !seq_len || !cand_idx || !cand_count || !topk_idx ||
         !topk_count)
@@ -544,8 +547,13 @@ extern "C" int lsa_topk(const float* rank_key, const int64_t* entry_start, const
                     need);
     int rc = check_device(nullptr);
     if (rc != LSA_OK) return rc;
-    hipLaunchKernelGGL(k_topk, dim3((unsigned)B), dim3(kTkThreads), 0, (hipStream_t)stream,
-                       rank_key, entry_start, seq_len, max_len, cand_idx, cand_count, k, topk_idx,
-                       topk_count, (uint32_t*)workspace);
+    if (out_positions)
+        hipLaunchKernelGGL(k_topk<true>, dim3((unsigned)B), dim3(kTkThreads), 0,
+                           (hipStream_t)stream, rank_key, entry_start, seq_len, max_len, cand_idx,
+                           cand_count, k, topk_idx, topk_count, (uint32_t*)workspace);
+    else
+        hipLaunchKernelGGL(k_topk<false>, dim3((unsigned)B), dim3(kTkThreads), 0,
+                           (hipStream_t)stream, rank_key, entry_start, seq_len, max_len, cand_idx,
+                           cand_count, k, topk_idx, topk_count, (uint32_t*)workspace);
     return launch_status("topk");
 }

@@ -124,6 +124,14 @@ class Pipeline:
         lsa.lsa_topk(self.r, d.entry_start, d.seq_len, d.max_len, self.cand_idx, self.cand_count,
                      d.k, self.topk_idx, self.topk_count, self.ws_topk, stream=stream)
 
+    def fetch(self, src, dst, stream=None):
+        """Just-in-time fetch: every kept entry's latent row of sequence b, from the
+        cold pool src (pinned host or device memory, laid out like the latent
+        pool), packed in list order into dst at latent_row_start[b]."""
+        d = self.d
+        lsa.lsa_fetch_rows(src, d.latent_row_start, self.cand_idx, d.entry_start, self.cand_count,
+                           d.max_len, dst, d.latent_row_start, stream=stream)
+
     def select(self, stream=None):
         d = self.d
         lsa.lsa_select_compact(self.z, d.entry_start, d.seq_len, d.max_len, self.cand_idx,

@@ -32,8 +32,8 @@ def lib():
 def test_header_declares_the_calls():
     syms = declared_symbols()
     for s in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
-              "lsa_sparse_attend", "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error",
-              "lsa_version"):
+              "lsa_fetch_rows", "lsa_sparse_attend", "lsa_workspace_bytes", "lsa_status_string",
+              "lsa_last_error", "lsa_version"):
         assert s in syms
     assert sorted(binding.EXPORTED) == syms
 
@@ -90,13 +90,33 @@ def test_select_validation(lib):
 def test_topk_validation(lib):
     P = FAKE
     f = lib.lsa_topk
-    assert f(P, P, P, 1, 10, P, P, 0, P, P, None, 0, None) == -1        # k = 0
-    assert f(P, P, P, 1, 10, P, P, -3, P, P, None, 0, None) == -1
-    assert f(P, P, P, 1, 10, P, P, 70000, P, P, None, 0, None) == -2    # k too large
-    assert f(None, P, P, 1, 10, P, P, 4, P, P, None, 0, None) == -1
+    assert f(P, P, P, 1, 10, P, P, 0, P, P, 0, None, 0, None) == -1        # k = 0
+    assert f(P, P, P, 1, 10, P, P, -3, P, P, 0, None, 0, None) == -1
+    assert f(P, P, P, 1, 10, P, P, 70000, P, P, 1, None, 0, None) == -2    # k too large
+    assert f(None, P, P, 1, 10, P, P, 4, P, P, 0, None, 0, None) == -1
     need = lib.lsa_workspace_bytes(2, 2, 0, 0, 0, 200000, 2048, 0)
     assert need > 0
-    assert f(P, P, P, 2, 200000, P, P, 2048, P, P, P, need - 4, None) == -3
+    assert f(P, P, P, 2, 200000, P, P, 2048, P, P, 0, P, need - 4, None) == -3
+
+
+def test_fetch_validation(lib):
+    P = FAKE
+    f = lib.lsa_fetch_rows
+    args = [P, 1024, P, P, P, P, 8, 20000, P, P, None]
+    for i in (0, 2, 3, 4, 5, 8, 9):                  # every required pointer
+        a = list(args); a[i] = None
+        assert f(*a) == -1, i
+    for i, v in ((1, 0), (1, 1000), (6, 0), (7, -1)):  # row_bytes, B, max_count
+        a = list(args); a[i] = v
+        assert f(*a) == -1, (i, v)
+    a = list(args); a[0] = MISALIGNED
+    assert f(*a) == -1
+    a = list(args); a[8] = MISALIGNED
+    assert f(*a) == -1
+    a = list(args); a[6] = 70000
+    assert f(*a) == -2
+    a = list(args); a[1] = 1 << 40
+    assert f(*a) == -2
 
 
 def test_attend_validation(lib):

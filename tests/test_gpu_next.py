@@ -1,12 +1,14 @@
-"""GPU parity of the two widened rows: the native re-score of the kept subset
-(lsa_index_rescore) and the OR-mode union over several indexers (lsa_index_score
-with reduce_max = 2), against the CPU reference on identical inputs."""
+"""GPU parity of the widened rows against the CPU reference on identical inputs:
+the native re-score of the kept subset (lsa_index_rescore), the OR-mode union
+over several indexers (lsa_index_score with reduce_max = 2), and the
+just-in-time fetch of the kept rows into a hot buffer (lsa_fetch_rows, with
+lsa_topk naming positions in the candidate list)."""
 import numpy as np
 import pytest
 import torch
 
-from gpu_util import (announce, check_scores, check_selection, check_topk, check_topk_properties,
-                      dev, host)
+from gpu_util import (announce, bf16_to_f64, check_attention, check_scores, check_selection,
+                      check_topk, check_topk_properties, dev, host)
 from lookahead_sparse_kv_amd import binding as lsa
 from lookahead_sparse_kv_amd import inputs
 
@@ -160,3 +162,148 @@ def test_union_over_indexers(ref, T, H, D, lens, dtype):
                                 wl.bias, reduce_max=True, want_prob=False, union_with=zr)
     torch.cuda.synchronize()
     check_scores(host(z), zr, host(p))
+
+
+# ------------------------------------------------- just-in-time fetch of the kept rows
+
+def _ws(op, B, *args, **kw):
+    return torch.empty(max(1, lsa.lsa_workspace_bytes(op, B, *args, **kw)), dtype=torch.uint8,
+                       device="cuda")
+
+
+@pytest.mark.parametrize("lens,k,frac", [
+    ([5000, 0, 37, 12000], 64, 0.6),       # register path, ragged, an empty sequence
+    ([3000, 3000], 2048, 0.9),
+    ([30], 64, 0.5),                       # fewer candidates than k: the whole list
+    ([100000, 50000], 1024, 0.5),          # > register capacity: global-key path
+])
+def test_topk_positions(ref, lens, k, frac):
+    """Positions mode: exactly the reference's positions, and cand[pos] is the
+    entry-index output of the same call without it."""
+    rng = np.random.default_rng(sum(lens) + k)
+    lens = np.asarray(lens, np.int32)
+    es, cand, cnt = _candidates(k, lens, frac)
+    r = rng.integers(-5, 60, size=max(1, int(lens.sum()))).astype(np.float32)   # many ties
+    B = len(lens)
+    ml = int(lens.max())
+    out = {}
+    for pos in (False, True):
+        ti = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
+        tc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        announce(f"topk positions={pos} lens={lens.tolist()} k={k}")
+        lsa.lsa_topk(dev(r), dev(es), dev(lens), ml, dev(cand), dev(cnt), k, ti, tc,
+                     _ws(lsa.LSA_OP_TOPK, B, max_len=ml, k=k), out_positions=pos)
+        torch.cuda.synchronize()
+        out[pos] = (host(ti), host(tc))
+    tr, tcr = ref.topk(r.astype(np.float64), es, lens, cand, cnt, k, positions=True)
+    (ti, tc), (pi, pc) = out[False], out[True]
+    np.testing.assert_array_equal(pc, tcr)
+    np.testing.assert_array_equal(tc, pc)
+    for b in range(B):
+        np.testing.assert_array_equal(pi[b, :pc[b]], tr[b, :tcr[b]])
+        np.testing.assert_array_equal(cand[es[b] + pi[b, :pc[b]]], ti[b, :tc[b]])
+        assert np.all(pi[b, pc[b]:] == -7), "entries past the count must be untouched"
+
+
+def _fetch_case(seed, lens, frac, width, pinned):
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int32)
+    es, cand, cnt = _candidates(seed + 1, lens, frac)
+    pool = rng.integers(0, 1 << 16, size=(max(1, int(lens.sum())), width), dtype=np.uint16)
+    src = torch.from_numpy(pool.view(np.int16)).view(torch.bfloat16)
+    src = src.pin_memory() if pinned else src.cuda()
+    drs = np.concatenate([[0], np.cumsum(cnt[:-1] + 3)]).astype(np.int64)   # gaps of 3 rows
+    n_dst = int(drs[-1] + cnt[-1] + 3)
+    init = rng.integers(0, 1 << 16, size=(n_dst, width), dtype=np.uint16)
+    return es, cand, cnt, pool, src, drs, init
+
+
+@pytest.mark.parametrize("pinned", [True, False])
+@pytest.mark.parametrize("lens,frac,width", [
+    ([5000, 37, 0, 2100], 0.3, 576),       # latent + rope row, ragged, an empty sequence
+    ([20000], 1.0, 576),                   # every entry: many tiles per sequence
+    ([700, 129], 0.5, 8),                  # one 16-byte segment per row
+    ([333, 90, 1], 0.4, 1000),             # 125 segments: a tile spans loop steps
+])
+def test_fetch_rows_bit_exact(ref, pinned, lens, frac, width):
+    es, cand, cnt, pool, src, drs, init = _fetch_case(len(lens) * width, lens, frac, width, pinned)
+    dst = dev(init)
+    announce(f"fetch pinned={pinned} lens={lens} frac={frac} width={width}")
+    lsa.lsa_fetch_rows(src, dev(es), dev(cand), dev(es), dev(cnt), int(cnt.max()), dst, dev(drs))
+    torch.cuda.synchronize()
+    want = ref.fetch_rows(pool, es, cand, es, cnt, len(init), drs, dst_init=init)
+    np.testing.assert_array_equal(host(dst), want)
+
+
+def test_fetch_refuses_pageable_source():
+    src = torch.zeros((64, 576), dtype=torch.bfloat16)           # pageable host memory
+    z64 = torch.zeros(1, dtype=torch.int64, device="cuda")
+    idx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cnt = torch.ones(1, dtype=torch.int32, device="cuda")
+    dst = torch.zeros((1, 576), dtype=torch.bfloat16, device="cuda")
+    lib = lsa.load_library()
+    announce("fetch from pageable host memory is refused")
+    rc = lib.lsa_fetch_rows(src.data_ptr(), 1152, z64.data_ptr(), idx.data_ptr(), z64.data_ptr(),
+                            cnt.data_ptr(), 1, 1, dst.data_ptr(), z64.data_ptr(), None)
+    assert rc == lsa.LSA_ERR_INVALID_ARG, lib.lsa_last_error().decode()
+    torch.cuda.synchronize()
+    assert torch.all(dst == 0)
+
+
+@pytest.mark.parametrize("B,Hq,Dl,lens,k,hca", [
+    (3, 64, 512, [9000, 2500, 40], 512, [300, 0, 17]),
+    (2, 64, 512, [40000, 1500], 2048, [900, 64]),
+    (2, 16, 128, [700, 3], 64, None),
+])
+def test_fetch_then_attend(ref, B, Hq, Dl, lens, k, hca):
+    """Gate, fetch every kept row from a pinned host pool into a hot buffer, take the
+    top-k as positions in the list and attend over the hot buffer: the output is
+    bit-identical to attention over the whole pool by entry index, and within the
+    attention tolerance of the reference."""
+    wl = inputs.random_small(B * 7 + Dl, B, 1, 64, 128, lens, k=k, Hq=Hq, Dl=Dl, hca_lens=hca,
+                             bias=-1.0)
+    z = torch.empty(wl.total_entries, device="cuda")
+    lsa.lsa_index_score(dev(wl.keys), dev(wl.key_row_start), dev(wl.seq_len), dev(wl.entry_start),
+                        wl.max_len, dev(wl.q), dev(wl.w), wl.bias, 1, z)
+    cand = torch.empty(wl.total_entries, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, dtype=torch.int32, device="cuda")
+    lsa.lsa_select_compact(z, dev(wl.entry_start), dev(wl.seq_len), wl.max_len, cand, cnt,
+                           _ws(lsa.LSA_OP_SELECT, B, max_len=wl.max_len))
+    wst = _ws(lsa.LSA_OP_TOPK, B, max_len=wl.max_len, k=k)
+    sel = {}
+    for pos in (False, True):
+        ti = torch.full((B, k), -1, dtype=torch.int32, device="cuda")
+        tc = torch.empty(B, dtype=torch.int32, device="cuda")
+        lsa.lsa_topk(z, dev(wl.entry_start), dev(wl.seq_len), wl.max_len, cand, cnt, k, ti, tc,
+                     wst, out_positions=pos)
+        sel[pos] = (ti, tc)
+    torch.cuda.synchronize()
+    cnt_h = host(cnt)
+    # hot buffer: sequence b's kept rows at hot_rs[b] ...
+    hot_rs = np.concatenate([[0], np.cumsum(cnt_h[:-1])]).astype(np.int64)
+    hot = torch.zeros((max(1, int(cnt_h.sum())), Dl), dtype=torch.bfloat16, device="cuda")
+    pool = dev(wl.latent, device="cpu").pin_memory()
+    announce(f"fetch->attend B={B} Hq={Hq} Dl={Dl} lens={lens} k={k} counts={cnt_h.tolist()}")
+    lsa.lsa_fetch_rows(pool, dev(wl.latent_row_start), cand, dev(wl.entry_start), cnt,
+                       int(max(1, cnt_h.max())), hot, dev(hot_rs))
+    use_hca = wl.hca is not None
+    outs = []
+    for latent, lrs, (ti, tc) in ((dev(wl.latent), dev(wl.latent_row_start), sel[False]),
+                                  (hot, dev(hot_rs), sel[True])):
+        out = torch.full((B, 1, Hq, Dl), float("nan"), dtype=torch.bfloat16, device="cuda")
+        lse = torch.full((B, 1, Hq), float("nan"), device="cuda")
+        lsa.lsa_sparse_attend(dev(wl.qa), latent, lrs, ti, tc, k, out,
+                              hca=dev(wl.hca) if use_hca else None,
+                              hca_row_start=dev(wl.hca_row_start) if use_hca else None,
+                              hca_count=dev(wl.hca_count) if use_hca else None,
+                              max_hca=wl.max_hca, scale=wl.scale, lse=lse,
+                              workspace=_ws(lsa.LSA_OP_ATTEND, B, 1, Hq, Dl, k=k,
+                                            max_hca=wl.max_hca))
+        torch.cuda.synchronize()
+        outs.append((host(out), host(lse)))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+    ti_h, tc_h = host(sel[False][0]), host(sel[False][1])
+    orf, lr = ref.sparse_attend(wl.qa, wl.latent, wl.latent_row_start, ti_h, tc_h, k, wl.hca,
+                                wl.hca_row_start, wl.hca_count, wl.scale)
+    check_attention(bf16_to_f64(outs[1][0]), orf, outs[1][1], lr)
