@@ -27,6 +27,45 @@ static double load_elem(const void* base, int dtype, int64_t i) {
 
 static int dtype_ok(int dtype) { return dtype == 0 || dtype == 1; }
 
+/* O0 -- TS 2.1 "Memory Indexer" and TS 2.3 "Query Optimization": two low-rank
+ * projections for the queries, one linear projection for the gate weights. */
+int lsa_ref_query_encode(const void* h, int dtype, int M, int d_model, int r, int H, int D,
+                         const void* w_down, const void* w_up, const void* w_gate,
+                         double* c_out, double* q_out, double* w_out) {
+    if (!h || !w_down || !w_up || !w_gate || !c_out || !q_out || !w_out) return -1;
+    if (M <= 0 || d_model <= 0 || r <= 0 || H <= 0 || D <= 0 || !dtype_ok(dtype)) return -1;
+    for (int m = 0; m < M; ++m) {
+        const int64_t hrow = (int64_t)m * d_model;
+        /* the low-rank latent of this token */
+        for (int i = 0; i < r; ++i) {
+            double acc = 0.0;
+            for (int k = 0; k < d_model; ++k)
+                acc += load_elem(w_down, dtype, (int64_t)i * d_model + k) *
+                       load_elem(h, dtype, hrow + k);
+            c_out[(int64_t)m * r + i] = acc;
+        }
+        /* each head's query from the latent */
+        for (int hd = 0; hd < H; ++hd) {
+            for (int d = 0; d < D; ++d) {
+                const int64_t urow = ((int64_t)hd * D + d) * r;
+                double acc = 0.0;
+                for (int i = 0; i < r; ++i)
+                    acc += load_elem(w_up, dtype, urow + i) * c_out[(int64_t)m * r + i];
+                q_out[((int64_t)m * H + hd) * D + d] = acc;
+            }
+        }
+        /* each head's gate weight from the hidden state */
+        for (int hd = 0; hd < H; ++hd) {
+            double acc = 0.0;
+            for (int k = 0; k < d_model; ++k)
+                acc += load_elem(w_gate, dtype, (int64_t)hd * d_model + k) *
+                       load_elem(h, dtype, hrow + k);
+            w_out[(int64_t)m * H + hd] = acc;
+        }
+    }
+    return 0;
+}
+
 /* O1 -- TS 2.1 "Scoring Mechanism"; dot-product interaction per TS 5. */
 int lsa_ref_index_score(const void* keys, int dtype, const int64_t* key_row_start,
                         const int32_t* seq_len, const int64_t* entry_start,

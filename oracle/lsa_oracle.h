@@ -85,6 +85,19 @@ int lsa_ref_topk(const double* r, const int64_t* entry_start, const int32_t* seq
                  int B, const int32_t* cand_idx, const int32_t* cand_count, int k,
                  int out_positions, int32_t* topk_idx, int32_t* topk_count);
 
+/* O0  Memory-Indexer query encoder (TS 2.1 "Memory Indexer": the query
+ * token's hidden state h_t mapped into low-rank indexer queries; TS 2.3
+ * "Query Optimization": low-rank projection matrices).  For token m:
+ *   c[m]       = W_down h[m]              rank r
+ *   q[m, h, :] = W_up[h*D .. h*D+D-1] c[m] D per indexer head
+ *   w[m, h]    = W_gate[h] . h[m]         the head's gate weight
+ * h [M, d_model], W_down [r, d_model], W_up [H*D, r], W_gate [H, d_model],
+ * all of dtype (0 fp32, 1 bf16) and row-major; outputs fp64 c [M, r],
+ * q [M, H, D], w [M, H]. */
+int lsa_ref_query_encode(const void* h, int dtype, int M, int d_model, int r, int H, int D,
+                         const void* w_down, const void* w_up, const void* w_gate,
+                         double* c_out, double* q_out, double* w_out);
+
 /* O5  Just-in-time fetch (TS 2.1 "Dynamic Fetching": the kept entries are
  * fetched from the CPU-side cold pool into GPU memory).  Row copy:
  *   dst row dst_row_start[b]+j = src row src_row_start[b] + idx[idx_start[b]+j]

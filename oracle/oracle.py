@@ -46,10 +46,12 @@ def _bind(path):
     lib.lsa_ref_select.argtypes = [P, P, P, I, D, P, P]
     lib.lsa_ref_topk.argtypes = [P, P, P, I, P, P, I, I, P, P]
     lib.lsa_ref_fetch_rows.argtypes = [P, ctypes.c_int64, P, P, P, P, I, P, P]
+    lib.lsa_ref_query_encode.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P]
     lib.lsa_ref_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, D, P, P]
     lib.lsa_ref_index_rescore.argtypes = [P, I, P, P, P, P, I, I, I, P, P, P]
     for f in (lib.lsa_ref_index_score, lib.lsa_ref_select, lib.lsa_ref_topk,
-              lib.lsa_ref_sparse_attend, lib.lsa_ref_index_rescore, lib.lsa_ref_fetch_rows):
+              lib.lsa_ref_sparse_attend, lib.lsa_ref_index_rescore, lib.lsa_ref_fetch_rows,
+              lib.lsa_ref_query_encode):
         f.restype = ctypes.c_int
     return lib
 
@@ -241,6 +243,26 @@ def sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k, hca=Non
                                    float(scale), _ptr(out), _ptr(lse))
     _check(rc, "sparse_attend")
     return out, lse
+
+
+def query_encode(h, w_down, w_up, w_gate, H, D):
+    """O0: c = W_down h, q[h] = W_up[h] c, w[h] = W_gate[h] . h per token (fp64).
+    h [M, d_model]; returns c [M, r], q [M, H, D], w [M, H]."""
+    lib = _load()
+    h = np.ascontiguousarray(h)
+    w_down, w_up, w_gate = (np.ascontiguousarray(a) for a in (w_down, w_up, w_gate))
+    dt = _dtype_code(h)
+    assert all(_dtype_code(a) == dt for a in (w_down, w_up, w_gate))
+    M, dm = h.shape
+    r = w_down.shape[0]
+    assert w_down.shape == (r, dm) and w_up.shape == (H * D, r) and w_gate.shape == (H, dm)
+    c = np.zeros((M, r))
+    q = np.zeros((M, H, D))
+    w = np.zeros((M, H))
+    rc = lib.lsa_ref_query_encode(_ptr(h), dt, M, dm, r, H, D, _ptr(w_down), _ptr(w_up),
+                                  _ptr(w_gate), _ptr(c), _ptr(q), _ptr(w))
+    _check(rc, "query_encode")
+    return c, q, w
 
 
 def fetch_rows(src, src_row_start, idx, idx_start, count, dst_rows, dst_row_start, dst_init=None):

@@ -46,6 +46,16 @@ MUTANTS = {
                                  "const int64_t to = j;"),
     "fetch_src_offset_dropped": ("const int64_t from = src_row_start[b] + idx[idx_start[b] + j];",
                                  "const int64_t from = idx[idx_start[b] + j];"),
+    "encoder_down_transposed": ("acc += load_elem(w_down, dtype, (int64_t)i * d_model + k) *",
+                                "acc += load_elem(w_down, dtype, (int64_t)k * r + i) *"),
+    "encoder_up_head_offset_dropped": ("const int64_t urow = ((int64_t)hd * D + d) * r;",
+                                       "const int64_t urow = ((int64_t)d) * r;"),
+    "encoder_gate_reads_down": ("acc += load_elem(w_gate, dtype, (int64_t)hd * d_model + k) *",
+                                "acc += load_elem(w_down, dtype, (int64_t)hd * d_model + k) *"),
+    "encoder_token_row_dropped": ("const int64_t hrow = (int64_t)m * d_model;",
+                                  "const int64_t hrow = 0;"),
+    "encoder_latent_of_token0": ("acc += load_elem(w_up, dtype, urow + i) * c_out[(int64_t)m * r + i];",
+                                 "acc += load_elem(w_up, dtype, urow + i) * c_out[i];"),
     "fetch_list_offset_dropped": ("const int64_t from = src_row_start[b] + idx[idx_start[b] + j];",
                                   "const int64_t from = src_row_start[b] + idx[j];"),
 }

@@ -521,3 +521,68 @@ def test_attention_over_fetched_rows_equals_attention_over_pool(ref):
     o1, l1 = ref.sparse_attend(qa, pool, es, t, tc, k, scale=0.2)
     o2, l2 = ref.sparse_attend(qa, hot, hot_rs, pos, pc, k, scale=0.2)
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------- query encoder (O0)
+
+def _onehot_rows(n_rows, n_cols, cols):
+    m = np.zeros((n_rows, n_cols), np.float32)
+    m[np.arange(n_rows), cols] = 1.0
+    return m
+
+
+def test_encoder_one_hot_weights_are_gathers(ref):
+    """One-hot weight rows turn every projection into a gather: c_i = h[pi(i)],
+    q[h, d] = c[sigma(h*D+d)], w[h] = h[rho(h)] -- exact, and sensitive to any
+    transposed or mis-offset index (all shapes differ)."""
+    rng = np.random.default_rng(31)
+    M, dm, r, H, D = 3, 11, 7, 2, 5
+    h = rng.standard_normal((M, dm)).astype(np.float32)
+    pi, sigma, rho = rng.integers(0, dm, r), rng.integers(0, r, H * D), rng.integers(0, dm, H)
+    c, q, w = ref.query_encode(h, _onehot_rows(r, dm, pi), _onehot_rows(H * D, r, sigma),
+                               _onehot_rows(H, dm, rho), H, D)
+    assert np.array_equal(c, h[:, pi].astype(np.float64))
+    assert np.array_equal(q, h[:, pi][:, sigma].reshape(M, H, D).astype(np.float64))
+    assert np.array_equal(w, h[:, rho].astype(np.float64))
+
+
+def test_encoder_identity_up_and_gate_reduce_to_matmul(ref):
+    """W_up = I (r = H*D): q is W_down h, a plain matmul; the gate is W_gate h."""
+    rng = np.random.default_rng(32)
+    M, dm, H, D = 4, 24, 3, 4
+    r = H * D
+    h = rng.standard_normal((M, dm)).astype(np.float32)
+    wd = rng.standard_normal((r, dm)).astype(np.float32)
+    wg = rng.standard_normal((H, dm)).astype(np.float32)
+    c, q, w = ref.query_encode(h, wd, np.eye(r, dtype=np.float32), wg, H, D)
+    want = h.astype(np.float64) @ wd.astype(np.float64).T
+    assert np.allclose(c, want, rtol=0, atol=1e-12)
+    assert np.allclose(q.reshape(M, r), want, rtol=0, atol=1e-12)
+    assert np.allclose(w, h.astype(np.float64) @ wg.astype(np.float64).T, rtol=0, atol=1e-12)
+
+
+def test_encoder_linear_and_token_separable(ref):
+    """The encoder is linear in h, and token m's outputs depend on row m only."""
+    rng = np.random.default_rng(33)
+    M, dm, r, H, D = 5, 16, 6, 2, 3
+    wd, wu, wg = (rng.integers(-3, 4, s).astype(np.float32) for s in ((r, dm), (H * D, r), (H, dm)))
+    h1, h2 = (rng.integers(-3, 4, (M, dm)).astype(np.float32) for _ in range(2))
+    o1, o2 = ref.query_encode(h1, wd, wu, wg, H, D), ref.query_encode(h2, wd, wu, wg, H, D)
+    o3 = ref.query_encode(2.0 * h1 - 3.0 * h2, wd, wu, wg, H, D)
+    for a, b, s in zip(o1, o2, o3):
+        assert np.array_equal(s, 2.0 * a - 3.0 * b)          # integers: exact
+    perm = rng.permutation(M)
+    op = ref.query_encode(h1[perm], wd, wu, wg, H, D)
+    for a, b in zip(o1, op):
+        assert np.array_equal(a[perm], b)
+
+
+def test_encoder_bf16_inputs_widen_exactly(ref):
+    rng = np.random.default_rng(34)
+    M, dm, r, H, D = 2, 8, 4, 2, 2
+    arrs = [rng.standard_normal(s).astype(np.float32) for s in ((M, dm), (r, dm), (H * D, r), (H, dm))]
+    bits = [(a.view(np.uint32) >> 16).astype(np.uint16) for a in arrs]
+    wide = [(b.astype(np.uint32) << 16).view(np.float32) for b in bits]
+    for x, y in zip(ref.query_encode(bits[0], bits[1], bits[2], bits[3], H, D),
+                    ref.query_encode(wide[0], wide[1], wide[2], wide[3], H, D)):
+        assert np.array_equal(x, y)
