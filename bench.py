@@ -87,6 +87,55 @@ def capture(torch, stream, fns):
     return g
 
 
+def encoder_setup(torch, lsa, inputs, wl, rotate):
+    """Encoder inputs for the workload's B*T tokens: weight replicas (enough to
+    rotate through ROTATE_BYTES if rotate), hidden states and output buffers."""
+    from lookahead_sparse_kv_amd.pipeline import _to_dev
+    H, D, rk = wl.H, wl.D, inputs.ENCODER_RANK
+    M = wl.B * wl.T
+    w0 = [_to_dev(x, "cuda") for x in inputs.encoder_weights(H, D)]
+    wbytes = sum(t.numel() * 2 for t in w0)
+    nrep = max(1, -(-ROTATE_BYTES // wbytes)) if rotate else 1
+    reps = [w0] + [[t.clone() for t in w0] for _ in range(nrep - 1)]
+    h = _to_dev(inputs.hidden_states(M), "cuda")
+    c = torch.empty((M, rk), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((M, H, D), dtype=torch.bfloat16, device="cuda")
+    w = torch.empty((M, H), dtype=torch.float32, device="cuda")
+
+    def call(i):
+        lsa.lsa_query_encode(h, *reps[i % nrep], H, D, c, q, w)
+    return call, reps, h, wbytes
+
+
+def time_encoder(torch, lsa, inputs, stream, wl, reps_for, args):
+    """Seconds per lsa_query_encode call for the workload's B*T tokens, and per pair
+    of torch.mm products of the same shapes; plus the sizes."""
+    H, D, dm, rk = wl.H, wl.D, inputs.ENCODER_D_MODEL, inputs.ENCODER_RANK
+    M = wl.B * wl.T
+    call, reps, h, wbytes = encoder_setup(torch, lsa, inputs, wl, rotate=True)
+    nrep = len(reps)
+    calls = [lambda i=i: call(i) for i in range(max(nrep, reps_for(2e-5)))]
+    t_enc = timed_graph(torch, stream, capture(torch, stream, calls), len(calls))
+    # library reference: [W_down; W_gate] and W_up, transposed once, contiguous
+    lib_w = [(torch.cat([r[0], r[2]]).t().contiguous(), r[1].t().contiguous()) for r in reps]
+    cw = torch.empty((M, rk + H), dtype=torch.bfloat16, device="cuda")
+    qq = torch.empty((M, H * D), dtype=torch.bfloat16, device="cuda")
+
+    def lib_pair(i):
+        a, b = lib_w[i % nrep]
+        torch.mm(h, a, out=cw)
+        torch.mm(cw[:, :rk], b, out=qq)
+    lib_pair(0)                   # the library sets itself up outside graph capture
+    torch.cuda.synchronize()
+    calls = [lambda i=i: lib_pair(i) for i in range(len(calls))]
+    t_lib = timed_graph(torch, stream, capture(torch, stream, calls), len(calls))
+    flops = 2.0 * M * (dm * (rk + H) + rk * H * D)
+    alg_bytes = wbytes + M * dm * 2 + 2 * M * rk * 2 + M * H * D * 2 + M * H * 4
+    del reps, lib_w
+    return {"t": t_enc, "t_lib": t_lib, "M": M, "flops": flops, "bytes": alg_bytes,
+            "d_model": dm, "rank": rk}
+
+
 def timed_eager(torch, stream, calls, launches, intervals=5, warm=1):
     """Median seconds per launch of `calls` (`launches` launches) issued eagerly on
     `stream`, for long launches whose issue cost is small beside their run time."""
@@ -183,6 +232,9 @@ def main():
                 p.step(i)
             for i in range(args.profile_launches):
                 p.rescore(i)
+            enc_call = encoder_setup(torch, lsa, inputs, wl, rotate=False)[0]
+            for i in range(args.profile_launches):
+                enc_call(i)
             if args.copy_bytes:
                 a = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
                 b = torch.empty_like(a)
@@ -236,6 +288,10 @@ def main():
         r = max(2, reps_for(step_s) // 3)
         t_union3 = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.score_union(3, 3 * i) for i in range(r)]), r)
+        # Memory-Indexer query encoder: the step's B*T hidden states -> q, w (weight
+        # replicas rotate, as a trigger finds them in HBM); beside it, the same two
+        # products through torch.mm (hipBLASLt), a library reference point
+        enc = time_encoder(torch, lsa, inputs, stream, wl, reps_for, args)
         p.score(0)
         p.select()
         # just-in-time fetch of the kept latent rows into a hot buffer, once per
@@ -343,6 +399,17 @@ def main():
         "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s", None),
         "cpu_baseline": None,
     }
+    t_e = enc["t"]
+    line["kernels_us"]["query_encode"] = round(t_e * 1e6, 2)
+    line["kernels_us"]["query_encode_torch_mm"] = round(enc["t_lib"] * 1e6, 2)
+    line["encoder"] = {"tokens": enc["M"], "d_model": enc["d_model"], "rank": enc["rank"],
+                       "heads": wl.H, "head_dim": wl.D}
+    if enc["M"] <= 64:   # few tokens: a stream of the weights
+        line["roofline_encode"] = roof("hbm", enc["bytes"], t_e, HBM_PEAK_GBS, "GB/s", None)
+    else:
+        line["roofline_encode"] = roof("mfma", enc["flops"], t_e, BF16_PEAK_TFLOPS, "TFLOP/s", None)
+    line["decode_tokens_per_s_tau64_with_encoder"] = round(
+        wl.B * wl.T / (t_attend + (t_e + t_score + t_select + t_topk) / 64.0), 1)
     if fetch is not None:
         t_fh, t_fd, t_h2d, pool_bytes, t_win, t_both = fetch
         fetched = int(counts.sum()) * wl.Dl * 2

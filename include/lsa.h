@@ -5,6 +5,9 @@
  * "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via Lookahead
  * Sparse Attention" (gist.science/paper/2606.09079), Technical Summary
  * section 2.1 "Architectural Design":
+ *   lsa_query_encode    -- the Memory Indexer's query encoder: hidden states
+ *                          to the score's per-head queries and gate weights
+ *                          ("Memory Indexer"; section 2.3);
  *   lsa_index_score     -- the Memory Indexer's lookahead index score I_{t,s}
  *                          against every preceding compressed entry ("Scoring
  *                          Mechanism"), with the OR-union over positions of
@@ -128,6 +131,27 @@ int lsa_index_rescore(const void* keys, int dtype, const int64_t* key_row_start,
                       const int32_t* cand_idx, const int32_t* cand_count, int B, int H, int D,
                       int64_t max_cand, const void* q, const float* w, float* r_out,
                       void* stream);
+
+/* Memory-Indexer query encoder (section 2.1 "Memory Indexer": the query
+ * token's hidden state h_t is mapped into low-rank indexer queries; section
+ * 2.3 "Query Optimization": the encoder's low-rank projection matrices).
+ * For each of the M tokens (M = B*T, in the score's (b, t) order):
+ *     c[m]       = W_down h[m]            rank r, rounded to bf16 in c_buf
+ *     q[m, h, :] = W_up[h*D .. h*D+D-1] c[m]
+ *     w[m, h]    = W_gate[h] . h[m]
+ * fp32 accumulation; q is rounded to bf16, w stays fp32 -- exactly the q and
+ * w that lsa_index_score takes.
+ *   h       bf16 [M, d_model] row-major (device).
+ *   w_down  bf16 [rank, d_model]; w_up bf16 [H*D, rank]; w_gate bf16 [H, d_model]:
+ *           one weight row per output feature, row-major (device).
+ *   c_buf   bf16 [M, rank], caller-owned; holds c on return.
+ *   q_out   bf16 [M, H, D]; w_out fp32 [M, H].
+ * Two launches on stream (the down and gate projections share the first).
+ * Envelope: d_model and rank multiples of 64; h, the weights and c_buf
+ * 16-byte aligned.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int lsa_query_encode(const void* h, int M, int d_model, int rank, int H, int D,
+                     const void* w_down, const void* w_up, const void* w_gate, void* c_buf,
+                     void* q_out, float* w_out, void* stream);
 
 /* Dynamic fetching (section 2.1): keep every entry with I >= 0.5, with no
  * fixed count.  I >= 0.5 holds exactly when z >= 0, so the gate is taken on

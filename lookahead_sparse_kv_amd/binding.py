@@ -27,7 +27,7 @@ LSA_OP_SELECT = 1
 LSA_OP_TOPK = 2
 LSA_OP_ATTEND = 3
 
-EXPORTED = ["lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+EXPORTED = ["lsa_query_encode", "lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
             "lsa_fetch_rows",
             "lsa_sparse_attend",
             "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
@@ -58,6 +58,7 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
     lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, I, P, Z, P]
     lib.lsa_fetch_rows.argtypes = [P, L, P, P, P, P, I, L, P, P, P]
+    lib.lsa_query_encode.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P]
     lib.lsa_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, L, F, P, P, P, Z, P]
     lib.lsa_workspace_bytes.argtypes = [I, I, I, I, I, L, I, L]
     lib.lsa_workspace_bytes.restype = Z
@@ -68,7 +69,7 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_version.argtypes = []
     lib.lsa_version.restype = I
     for name in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
-                 "lsa_fetch_rows",
+                 "lsa_fetch_rows", "lsa_query_encode",
                  "lsa_sparse_attend"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -196,6 +197,27 @@ def lsa_topk(rank_key, entry_start, seq_len, max_len: int, cand_idx, cand_count,
                       1 if out_positions else 0, _ptr(workspace), ws_bytes, _stream(stream))
     _check("lsa_topk", rc)
     return topk_idx, topk_count
+
+
+def lsa_query_encode(h, w_down, w_up, w_gate, H: int, D: int, c_buf, q_out, w_out, stream=None):
+    """Memory-Indexer query encoder (see include/lsa.h): h [M, d_model] bf16 to the
+    score's q [M, H, D] bf16 and w [M, H] fp32, through the rank-r latent c_buf."""
+    lib = load_library()
+    for t, n in ((h, "h"), (w_down, "w_down"), (w_up, "w_up"), (w_gate, "w_gate"),
+                 (c_buf, "c_buf"), (q_out, "q_out")):
+        _dev(t, n, torch.bfloat16)
+    _dev(w_out, "w_out", torch.float32)
+    M, d_model = h.shape
+    rank = w_down.shape[0]
+    if (w_down.shape != (rank, d_model) or w_up.shape != (H * D, rank)
+            or w_gate.shape != (H, d_model)):
+        raise ValueError("lsa_query_encode: weight shapes do not match h, H and D")
+    if c_buf.numel() < M * rank or q_out.numel() < M * H * D or w_out.numel() < M * H:
+        raise ValueError("lsa_query_encode: an output buffer is too small")
+    rc = lib.lsa_query_encode(_ptr(h), M, d_model, rank, int(H), int(D), _ptr(w_down), _ptr(w_up),
+                              _ptr(w_gate), _ptr(c_buf), _ptr(q_out), _ptr(w_out), _stream(stream))
+    _check("lsa_query_encode", rc)
+    return q_out, w_out
 
 
 def lsa_fetch_rows(src, src_row_start, idx, idx_start, count, max_count: int, dst, dst_row_start,

@@ -17,7 +17,8 @@ LIB = os.path.join(HERE, "liblsa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["host_common.cpp", "score.hip", "rescore.hip", "select.hip", "topk.hip", "fetch.hip",
+SOURCES = ["host_common.cpp", "encode.hip", "score.hip", "rescore.hip", "select.hip", "topk.hip",
+           "fetch.hip",
            "attend.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

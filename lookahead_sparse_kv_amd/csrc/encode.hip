@@ -1,0 +1,280 @@
+// encode.hip -- lsa_query_encode: the Memory Indexer's query encoder.
+//
+// Page "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via
+// Lookahead Sparse Attention", Technical Summary 2.1 "Memory Indexer" (the query
+// token's hidden state h_t is mapped into low-rank indexer queries) and 2.3
+// "Query Optimization" (the encoder's low-rank projection matrices).  Per token m:
+//     c[m]    = W_down h[m]            rank r, kept in bf16 between the products
+//     q[m, h] = W_up[h] c[m]           bf16: the score's per-head queries
+//     w[m, h] = W_gate[h] . h[m]       fp32: the score's per-head gate weights
+//
+// Two launches of one product D = A B^T, A [M, K] activations and B [N, K]
+// weight rows, both bf16 with K contiguous, fp32 accumulation on the matrix
+// cores:
+//     1) A = h, B = [W_down ; W_gate] (N = r + H): columns < r go to c (bf16),
+//        the others to w (fp32) -- the gate rides along the down projection;
+//     2) A = c, B = W_up (N = H*D): q (bf16).
+// Few tokens (decode: one per sequence) make each product a stream of the
+// weights, bound by HBM: k_encode_skinny gives every workgroup 16 weight rows
+// and splits K over its waves, each wave holding all the tokens' rows in
+// registers, so every weight byte is read once.  Many tokens (a burst of tau
+// positions): k_encode_tiled, an LDS-tiled product bound by the matrix cores.
+#include "common.hpp"
+
+namespace lsa {
+
+// D = A B^T with column routing: weight row n < nsplit comes from b0 (row n)
+// and its output goes to out0 (bf16); row n >= nsplit comes from b1 (row
+// n - nsplit) and goes to out1 (fp32, column n - nsplit).
+struct EncGemm {
+    const bf16* a;
+    int64_t lda;
+    const bf16* b0;
+    const bf16* b1;
+    int M, N, K, nsplit;
+    bf16* out0;
+    int64_t ld0;
+    float* out1;
+    int64_t ld1;
+};
+
+__device__ __forceinline__ const bf16* enc_brow(const EncGemm& g, int n) {
+    return n < g.nsplit ? g.b0 + (int64_t)n * g.K : g.b1 + (int64_t)(n - g.nsplit) * g.K;
+}
+
+__device__ __forceinline__ void enc_store(const EncGemm& g, int m, int n, float v) {
+    if (n < g.nsplit)
+        g.out0[(int64_t)m * g.ld0 + n] = (bf16)v;
+    else
+        g.out1[(int64_t)m * g.ld1 + (n - g.nsplit)] = v;
+}
+
+// ------------------------------------------------------------- few tokens
+// Workgroup: weight rows n0 .. n0+15; wave w takes an even share of the K
+// steps (32 deep) and keeps U steps of loads in flight; MT tiles of 16 token
+// rows share each weight fragment.  The waves' partial sums meet in LDS and are
+// added in wave order (deterministic).  Rows past M or N are computed on a
+// clamped row and never stored.
+template <int MT, int WAVES, int U>
+__global__ __launch_bounds__(WAVES * kWave) void k_encode_skinny(EncGemm g) {
+    __shared__ float red[WAVES][MT][4][kWave];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n0 = blockIdx.x * 16;
+    const bf16* brow = enc_brow(g, min(n0 + (lane & 15), g.N - 1));
+    const bf16* arow[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) arow[t] = g.a + (int64_t)min(16 * t + (lane & 15), g.M - 1) * g.lda;
+    const int kq = 8 * (lane >> 4);
+    const int steps = g.K / 32;
+    const int s0 = steps * wave / WAVES, s1 = steps * (wave + 1) / WAVES;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = s0; s < s1; s += U) {
+        bf16x8 bv[U], av[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s + u < s1) {
+                const int k = 32 * (s + u) + kq;
+                bv[u] = load8(brow + k);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) av[u][t] = load8(arow[t] + k);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s + u < s1) {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[t] = mfma16(av[u][t], bv[u], acc[t]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[wave][t][v][lane] = acc[t][v];
+    __syncthreads();
+    for (int e = threadIdx.x; e < MT * 4 * kWave; e += WAVES * kWave) {
+        const int t = e / (4 * kWave), v = (e / kWave) & 3, l = e & 63;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) sum += red[w][t][v][l];
+        const int m = 16 * t + 4 * (l >> 4) + v, n = n0 + (l & 15);
+        if (m < g.M && n < g.N) enc_store(g, m, n, sum);
+    }
+}
+
+// ------------------------------------------------------------ many tokens
+// Workgroup tile (64 WM) x (64 WN), four waves in a 2 x 2 grid, each owning a
+// (32 WM) x (32 WN) block of 32x32x16 matrix-core tiles.  K advances 64 at a
+// time through two LDS buffers: the next slice is loaded into registers while
+// the current one is multiplied, then stored to the other buffer; one barrier
+// per slice.  LDS rows are padded to 72 elements (144 B) so the 16-byte
+// fragment reads of consecutive rows start on distinct banks.  Tiles are dealt
+// to XCDs in contiguous ranges, token tiles fastest, so the workgroups of one
+// XCD share both their activation and their weight rows in its L2.
+constexpr int kEncBK = 64;
+constexpr int kEncLdk = kEncBK + 8;
+
+template <int WM, int WN>
+__global__ __launch_bounds__(256) void k_encode_tiled(EncGemm g, int tiles_m, int tiles_n) {
+    constexpr int BM = 64 * WM, BN = 64 * WN;
+    constexpr int AL = BM / 32, BL = BN / 32;      // 16-byte loads per thread per slice
+    __shared__ __attribute__((aligned(16))) bf16 As[2][BM * kEncLdk];
+    __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * kEncLdk];
+
+    const int n_tiles = tiles_m * tiles_n;
+    const int per_xcd = (n_tiles + 7) / 8;
+    const int slot = blockIdx.x >> 3;
+    const int tile = (blockIdx.x & 7) * per_xcd + slot;
+    if (slot >= per_xcd || tile >= n_tiles) return;
+    const int m0 = (tile % tiles_m) * BM, n0 = (tile / tiles_m) * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = (wave & 1) * 32 * WM, wn = (wave >> 1) * 32 * WN;
+    const int seg = tid & 7, row0 = tid >> 3;      // 8 threads cover one 128-byte row slice
+    const bf16* ap[AL];
+    const bf16* bp[BL];
+#pragma unroll
+    for (int i = 0; i < AL; ++i)
+        ap[i] = g.a + (int64_t)min(m0 + row0 + 32 * i, g.M - 1) * g.lda + 8 * seg;
+#pragma unroll
+    for (int i = 0; i < BL; ++i) bp[i] = enc_brow(g, min(n0 + row0 + 32 * i, g.N - 1)) + 8 * seg;
+
+    u32x4 ra[AL], rb[BL];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + kt * kEncBK);
+#pragma unroll
+        for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + kt * kEncBK);
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < AL; ++i)
+            *reinterpret_cast<u32x4*>(&As[buf][(row0 + 32 * i) * kEncLdk + 8 * seg]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < BL; ++i)
+            *reinterpret_cast<u32x4*>(&Bs[buf][(row0 + 32 * i) * kEncLdk + 8 * seg]) = rb[i];
+    };
+
+    f32x16 acc[WM][WN];
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    const int nk = g.K / kEncBK;
+    const int fr = lane & 31, fk = 8 * (lane >> 5);
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < nk) gload(kt + 1);
+#pragma unroll
+        for (int ks = 0; ks < kEncBK / 16; ++ks) {
+            bf16x8 af[WM], bfr[WN];
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(
+                    &As[buf][(wm + 32 * i + fr) * kEncLdk + 16 * ks + fk]);
+#pragma unroll
+            for (int j = 0; j < WN; ++j)
+                bfr[j] = *reinterpret_cast<const bf16x8*>(
+                    &Bs[buf][(wn + 32 * j + fr) * kEncLdk + 16 * ks + fk]);
+#pragma unroll
+            for (int i = 0; i < WM; ++i)
+#pragma unroll
+                for (int j = 0; j < WN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
+        }
+        if (kt + 1 < nk) sstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    // lane l holds rows 8(v/4) + 4(l/32) + v%4, column l%32 of each 32x32 block
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+        for (int j = 0; j < WN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+                const int n = n0 + wn + 32 * j + (lane & 31);
+                if (m < g.M && n < g.N) enc_store(g, m, n, acc[i][j][v]);
+            }
+}
+
+constexpr int kEncSkinnyMaxM = 32;   // token rows the few-token kernel keeps in registers
+
+static int launch_product(const EncGemm& g, int num_cus, hipStream_t st) {
+    if (g.M <= kEncSkinnyMaxM) {
+        const dim3 grid((unsigned)ceil_div(g.N, 16));
+        // long K: 16 waves share it, so more weight loads are in flight per row block
+        if (g.M <= 16) {
+            if (g.K >= 4096)
+                hipLaunchKernelGGL((k_encode_skinny<1, 16, 8>), grid, dim3(16 * kWave), 0, st, g);
+            else
+                hipLaunchKernelGGL((k_encode_skinny<1, 8, 8>), grid, dim3(8 * kWave), 0, st, g);
+        } else {
+            if (g.K >= 4096)
+                hipLaunchKernelGGL((k_encode_skinny<2, 16, 8>), grid, dim3(16 * kWave), 0, st, g);
+            else
+                hipLaunchKernelGGL((k_encode_skinny<2, 8, 8>), grid, dim3(8 * kWave), 0, st, g);
+        }
+        return launch_status("query_encode");
+    }
+    // the large tile when it alone fills every CU, else the small one
+    const int tm2 = (int)ceil_div(g.M, 128), tn2 = (int)ceil_div(g.N, 128);
+    if ((int64_t)tm2 * tn2 >= num_cus) {
+        const unsigned grid = (unsigned)(8 * ceil_div((int64_t)tm2 * tn2, 8));
+        hipLaunchKernelGGL((k_encode_tiled<2, 2>), dim3(grid), dim3(256), 0, st, g, tm2, tn2);
+    } else {
+        const int tm = (int)ceil_div(g.M, 64), tn = (int)ceil_div(g.N, 64);
+        const unsigned grid = (unsigned)(8 * ceil_div((int64_t)tm * tn, 8));
+        hipLaunchKernelGGL((k_encode_tiled<1, 1>), dim3(grid), dim3(256), 0, st, g, tm, tn);
+    }
+    return launch_status("query_encode");
+}
+
+}  // namespace lsa
+
+using namespace lsa;
+
+extern "C" int lsa_query_encode(const void* h, int M, int d_model, int rank, int H, int D,
+                                const void* w_down, const void* w_up, const void* w_gate,
+                                void* c_buf, void* q_out, float* w_out, void* stream) {
+    clear_error();
+    if (!h || !w_down || !w_up || !w_gate || !c_buf || !q_out || !w_out)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_query_encode: a required pointer is NULL");
+    if (M <= 0 || d_model <= 0 || rank <= 0 || H <= 0 || D <= 0)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_query_encode: M=%d d_model=%d rank=%d H=%d D=%d", M,
+                    d_model, rank, H, D);
+    if (!aligned16(h) || !aligned16(w_down) || !aligned16(w_up) || !aligned16(w_gate) ||
+        !aligned16(c_buf))
+        return fail(LSA_ERR_INVALID_ARG,
+                    "lsa_query_encode: h, the weights and c_buf must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(q_out) & 1u) || (reinterpret_cast<uintptr_t>(w_out) & 3u))
+        return fail(LSA_ERR_INVALID_ARG, "lsa_query_encode: q_out or w_out misaligned");
+    if (d_model % 64 != 0 || rank % 64 != 0)
+        return fail(LSA_ERR_UNSUPPORTED,
+                    "lsa_query_encode: d_model=%d and rank=%d must be multiples of 64", d_model,
+                    rank);
+    if ((int64_t)H * D > (1 << 20) || (int64_t)rank + H > (1 << 20) || d_model > (1 << 20))
+        return fail(LSA_ERR_UNSUPPORTED, "lsa_query_encode: projection too large");
+    int num_cus = 0;
+    int rc = check_device(&num_cus);
+    if (rc != LSA_OK) return rc;
+    const hipStream_t st = (hipStream_t)stream;
+    const EncGemm down{(const bf16*)h,   d_model,         (const bf16*)w_down, (const bf16*)w_gate,
+                       M,                rank + H,        d_model,             rank,
+                       (bf16*)c_buf,     rank,            w_out,               H};
+    const EncGemm up{(const bf16*)c_buf, rank,  (const bf16*)w_up, (const bf16*)w_up,
+                     M,                  H * D, rank,              H * D,
+                     (bf16*)q_out,       H * D, nullptr,           0};
+    if ((rc = launch_product(down, num_cus, st)) != LSA_OK) return rc;
+    return launch_product(up, num_cus, st);
+}

@@ -306,6 +306,39 @@ def native_queries(wl: Workload, seed: int = 104729):
     return (to_bf16_bits(q) if wl.dtype == "bf16" else q), w
 
 
+# Memory-Indexer query encoder sizes.  The pages give neither the hidden size of
+# the backbone nor the encoder's rank; these are a DeepSeek-class hidden size and
+# a query low-rank dimension of the same family, chosen for the benchmark.
+ENCODER_D_MODEL = 7168
+ENCODER_RANK = 1536
+
+
+def encoder_weights(H: int, D: int, d_model: int = ENCODER_D_MODEL, rank: int = ENCODER_RANK,
+                    seed: int = 8191, int_valued: bool = False):
+    """Random (untrained) encoder weights as bf16 bits, one row per output feature:
+    W_down [rank, d_model] ~ N(0, 1/d_model), W_up [H*D, rank] ~ N(0, 1/(rank*D)),
+    W_gate [H, d_model] ~ N(0, 1/(4 d_model)), so that hidden states ~ N(0, 1) give
+    c ~ N(0, 1), q ~ N(0, 1/D) (the score's query scale) and w ~ N(0, 1/4).
+    int_valued: entries in {-1, 0, 1} (90 % zeros), for exact products."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, d_model, rank, H, D])))
+    shapes = ((rank, d_model), (H * D, rank), (H, d_model))
+    if int_valued:
+        return [to_bf16_bits((rng.integers(-1, 2, s) * (rng.random(s) < 0.1)).astype(np.float32))
+                for s in shapes]
+    sd = (1.0 / np.sqrt(d_model), 1.0 / np.sqrt(rank * D), 0.5 / np.sqrt(d_model))
+    return [to_bf16_bits(_normal(rng, s, sd_i)) for s, sd_i in zip(shapes, sd)]
+
+
+def hidden_states(M: int, d_model: int = ENCODER_D_MODEL, seed: int = 524287,
+                  int_valued: bool = False) -> np.ndarray:
+    """Hidden states h [M, d_model] ~ N(0, 1) as bf16 bits (int_valued: {-1, 0, 1},
+    a third each)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, M, d_model])))
+    if int_valued:
+        return to_bf16_bits(rng.integers(-1, 2, (M, d_model)).astype(np.float32))
+    return to_bf16_bits(_normal(rng, (M, d_model), 1.0))
+
+
 def random_small(seed: int, B: int, T: int, H: int, D: int, lens, dtype: str = "bf16",
                  k: int = 16, Hq: int = 16, Dl: int = 128, hca_lens=None, bias: float = 0.0,
                  shared: bool = False, w_low: float = 0.0, int_valued: bool = False) -> Workload:

@@ -31,9 +31,9 @@ def lib():
 
 def test_header_declares_the_calls():
     syms = declared_symbols()
-    for s in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
-              "lsa_fetch_rows", "lsa_sparse_attend", "lsa_workspace_bytes", "lsa_status_string",
-              "lsa_last_error", "lsa_version"):
+    for s in ("lsa_query_encode", "lsa_index_score", "lsa_index_rescore", "lsa_select_compact",
+              "lsa_topk", "lsa_fetch_rows", "lsa_sparse_attend", "lsa_workspace_bytes",
+              "lsa_status_string", "lsa_last_error", "lsa_version"):
         assert s in syms
     assert sorted(binding.EXPORTED) == syms
 
@@ -97,6 +97,24 @@ def test_topk_validation(lib):
     need = lib.lsa_workspace_bytes(2, 2, 0, 0, 0, 200000, 2048, 0)
     assert need > 0
     assert f(P, P, P, 2, 200000, P, P, 2048, P, P, 0, P, need - 4, None) == -3
+
+
+def test_encode_validation(lib):
+    P = FAKE
+    f = lib.lsa_query_encode
+    args = [P, 8, 7168, 1536, 64, 128, P, P, P, P, P, P, None]
+    for i in (0, 6, 7, 8, 9, 10, 11):                 # every required pointer
+        a = list(args); a[i] = None
+        assert f(*a) == -1, i
+    for i in (1, 2, 3, 4, 5):                          # M, d_model, rank, H, D
+        a = list(args); a[i] = 0
+        assert f(*a) == -1, i
+    a = list(args); a[0] = MISALIGNED                  # h not 16-byte aligned
+    assert f(*a) == -1
+    a = list(args); a[2] = 7168 + 32                   # d_model not a multiple of 64
+    assert f(*a) == -2
+    a = list(args); a[3] = 1000                        # rank not a multiple of 64
+    assert f(*a) == -2
 
 
 def test_fetch_validation(lib):
