@@ -40,9 +40,6 @@ constexpr int kAttRing = 4;         // ring slots of kChunk rows
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;  // keep the running max unless it grows by > 2^8
-// Fourth word of a raw buffer resource (32-bit data format, no swizzle, no
-// stride): the loads below use it with a byte offset and a range of one row.
-constexpr int kBufferWord3 = 0x00020000;
 
 // Row pointer of attended row j of sequence b (nullptr past the end).
 template <typename E>
@@ -96,22 +93,6 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (RG >= 8) x += dpp_mov<0x141>(x);
     if constexpr (RG >= 16) x += dpp_mov<0x140>(x);
     return x;
-}
-
-// vmcnt(n) with the other counters left alone (n <= 63).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Workgroup barrier for LDS traffic only: this wave's LDS operations retire
-// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for
-// outstanding global loads, so the direct-to-LDS copies of later chunks stay in
-// flight across it; each wave waits for its own copies with wait_vmcnt first.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0), vmcnt and expcnt left alone
-    __builtin_amdgcn_s_barrier();
 }
 
 // Parameter order: what the first loads need comes first (14 dwords: the work

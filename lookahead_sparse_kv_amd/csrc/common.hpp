@@ -42,6 +42,27 @@ __device__ __forceinline__ bf16x8 zero8() {
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// Word 3 of a buffer resource for plain raw buffer loads on gfx950; a load
+// past num_records (or through a range of 0) reads no memory.
+constexpr int kBufferWord3 = 0x00020000;
+
+// Wait until at most N of this wave's vector-memory loads are outstanding
+// (they complete in issue order); LDS and export counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations retire
+// (lgkmcnt(0)), then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding global loads, so copies of later data stay in flight across it;
+// a wave that copies into LDS waits for its own copies with wait_vmcnt first.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+}
+
 // ------------------------------------------------------------------ host side
 // Thread-local detail string for lsa_last_error(); returns `status`.
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));

@@ -21,6 +21,31 @@
 // positions): k_encode_tiled, an LDS-tiled product bound by the matrix cores.
 #include "common.hpp"
 
+// LDS stages of the tiled product per tile shape
+#ifndef LSA_ENC_NS22
+#define LSA_ENC_NS22 2
+#endif
+#ifndef LSA_ENC_NS21
+#define LSA_ENC_NS21 4
+#endif
+#ifndef LSA_ENC_NS11
+#define LSA_ENC_NS11 4
+#endif
+// K depth of one stage per tile shape (64 or 32)
+#ifndef LSA_ENC_BK22
+#define LSA_ENC_BK22 64
+#endif
+#ifndef LSA_ENC_BK21
+#define LSA_ENC_BK21 64
+#endif
+#ifndef LSA_ENC_BK11
+#define LSA_ENC_BK11 64
+#endif
+// 128x64 tiles are taken when they fill at least this percentage of the CUs
+#ifndef LSA_ENC_FILL21
+#define LSA_ENC_FILL21 75
+#endif
+
 namespace lsa {
 
 // D = A B^T with column routing: weight row n < nsplit comes from b0 (row n)
@@ -107,22 +132,37 @@ __global__ __launch_bounds__(WAVES * kWave) void k_encode_skinny(EncGemm g) {
 
 // ------------------------------------------------------------ many tokens
 // Workgroup tile (64 WM) x (64 WN), four waves in a 2 x 2 grid, each owning a
-// (32 WM) x (32 WN) block of 32x32x16 matrix-core tiles.  K advances 64 at a
-// time through two LDS buffers: the next slice is loaded into registers while
-// the current one is multiplied, then stored to the other buffer; one barrier
-// per slice.  LDS rows are padded to 72 elements (144 B) so the 16-byte
-// fragment reads of consecutive rows start on distinct banks.  Tiles are dealt
-// to XCDs in contiguous ranges, token tiles fastest, so the workgroups of one
-// XCD share both their activation and their weight rows in its L2.
-constexpr int kEncBK = 64;
-constexpr int kEncLdk = kEncBK + 8;
+// (32 WM) x (32 WN) block of 32x32x16 matrix-core tiles.  K advances BK at a
+// time through a ring of NS LDS stages that buffer loads fill directly
+// (`buffer_load ... lds`, no register staging): while stage kt is multiplied,
+// stages kt+1 .. kt+NS-2 are in flight and kt+NS-1 is issued.  One LDS-only
+// barrier per stage.  Each copy instruction writes 1 KiB of whole stage rows
+// and picks per lane which logical slot to fetch, so that slot s of row r sits
+// at s ^ swz(r) and the sixteen rows one fragment read touches at a time fall
+// in sixteen distinct 4-bank groups (measured: no bank conflicts).  Every
+// copy's buffer is settled before the loop, so the loop holds no branches
+// (a branch per copy costs the compiler's precise load counting and a third
+// of the speed).  Copies past the last stage use an empty range and read
+// nothing.  Tiles are dealt to XCDs in contiguous ranges, token tiles fastest,
+// so the workgroups of one XCD share their activation and weight rows in L2.
+// Measured at 1024 tokens (7168 -> 1536 -> 64 x 128): 64-deep stages beat
+// 32-deep ones; two stages and two workgroups per CU beat deeper rings with
+// one workgroup per CU on 128 x 128 tiles.
+template <int SLOTS>
+__device__ __forceinline__ int enc_swz(int row) {
+    return (row >> (SLOTS == 8 ? 1 : 2)) & (SLOTS - 1);
+}
 
-template <int WM, int WN>
+template <int WM, int WN, int NS, int BK>
 __global__ __launch_bounds__(256) void k_encode_tiled(EncGemm g, int tiles_m, int tiles_n) {
     constexpr int BM = 64 * WM, BN = 64 * WN;
-    constexpr int AL = BM / 32, BL = BN / 32;      // 16-byte loads per thread per slice
-    __shared__ __attribute__((aligned(16))) bf16 As[2][BM * kEncLdk];
-    __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN * kEncLdk];
+    constexpr int SLOTS = BK / 8;                  // 16-byte slots per stage row
+    constexpr int RPI = 64 / SLOTS;                // stage rows per copy instruction
+    constexpr int AL = BM / (4 * RPI), BL = BN / (4 * RPI);   // copies per wave per stage
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(AL >= 1 && BL >= 1, "tile too small for the copy layout");
+    static_assert((NS - 2) * (AL + BL) < 64 && NS >= 2, "vmcnt range");
+    __shared__ __attribute__((aligned(1024))) bf16 ring[NS][(BM + BN) * BK];
 
     const int n_tiles = tiles_m * tiles_n;
     const int per_xcd = (n_tiles + 7) / 8;
@@ -134,29 +174,60 @@ __global__ __launch_bounds__(256) void k_encode_tiled(EncGemm g, int tiles_m, in
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = (wave & 1) * 32 * WM, wn = (wave >> 1) * 32 * WN;
-    const int seg = tid & 7, row0 = tid >> 3;      // 8 threads cover one 128-byte row slice
-    const bf16* ap[AL];
-    const bf16* bp[BL];
-#pragma unroll
-    for (int i = 0; i < AL; ++i)
-        ap[i] = g.a + (int64_t)min(m0 + row0 + 32 * i, g.M - 1) * g.lda + 8 * seg;
-#pragma unroll
-    for (int i = 0; i < BL; ++i) bp[i] = enc_brow(g, min(n0 + row0 + 32 * i, g.N - 1)) + 8 * seg;
+    const int nk = g.K / BK;
 
-    u32x4 ra[AL], rb[BL];
-    auto gload = [&](int kt) {
+    // Wave w copies stage rows RPI (AL w + i) .. of A (i < AL) and RPI (BL w + j)
+    // .. of B (j < BL), one instruction each.  Per lane: the row's byte offset
+    // (clamped rows re-read the last one) at the logical slot it fetches.  Per
+    // B instruction: its buffer (weight rows below nsplit, or from nsplit; the
+    // first row decides, as nsplit is a multiple of RPI) and byte range, set
+    // once here so that the copies themselves hold no branches.
+    const int range_a = (int)min((int64_t)g.M * g.lda * 2, (int64_t)0x7fffffff);
+    uint32_t aoff[AL], boff[BL];
+    const bf16* bbase[BL];
+    int brange[BL];
 #pragma unroll
-        for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const u32x4*>(ap[i] + kt * kEncBK);
+    for (int i = 0; i < AL; ++i) {
+        const int r = RPI * (AL * wave + i) + lane / SLOTS;
+        const int m = min(m0 + r, g.M - 1);
+        aoff[i] = (uint32_t)(((int64_t)m * g.lda + 8 * ((lane % SLOTS) ^ enc_swz<SLOTS>(r))) * 2);
+    }
 #pragma unroll
-        for (int i = 0; i < BL; ++i) rb[i] = *reinterpret_cast<const u32x4*>(bp[i] + kt * kEncBK);
-    };
-    auto sstore = [&](int buf) {
+    for (int j = 0; j < BL; ++j) {
+        const int r8 = RPI * (BL * wave + j);
+        const int r = r8 + lane / SLOTS;
+        const bool hi = min(n0 + r8, g.N - 1) >= g.nsplit;
+        const int n = min(n0 + r, g.N - 1) - (hi ? g.nsplit : 0);
+        boff[j] = (uint32_t)(((int64_t)n * g.K + 8 * ((lane % SLOTS) ^ enc_swz<SLOTS>(BM + r))) * 2);
+        bbase[j] = hi ? g.b1 : g.b0;
+        brange[j] = (int)min((int64_t)(hi ? g.N - g.nsplit : g.nsplit) * g.K * 2,
+                             (int64_t)0x7fffffff);
+    }
+    auto issue = [&](int kt) {
+        const bool live = kt < nk;
+        const int soff = live ? kt * BK * 2 : 0;
+        bf16* st = ring[kt % NS];
 #pragma unroll
-        for (int i = 0; i < AL; ++i)
-            *reinterpret_cast<u32x4*>(&As[buf][(row0 + 32 * i) * kEncLdk + 8 * seg]) = ra[i];
+        for (int i = 0; i < AL; ++i) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)g.a, (short)0, live ? range_a : 0, kBufferWord3);
+            // read into a scalar first: passed as an array element, the host pass
+            // drops the kernel's launch stub
+            const uint32_t vo = aoff[i];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(st + RPI * (AL * wave + i) * BK),
+                16, vo, soff, 0, 0);
+        }
 #pragma unroll
-        for (int i = 0; i < BL; ++i)
-            *reinterpret_cast<u32x4*>(&Bs[buf][(row0 + 32 * i) * kEncLdk + 8 * seg]) = rb[i];
+        for (int j = 0; j < BL; ++j) {
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)bbase[j], (short)0, live ? brange[j] : 0, kBufferWord3);
+            const uint32_t vo = boff[j];
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs,
+                (__attribute__((address_space(3))) void*)(st + (BM + RPI * (BL * wave + j)) * BK),
+                16, vo, soff, 0, 0);
+        }
     };
 
     f32x16 acc[WM][WN];
@@ -167,33 +238,36 @@ __global__ __launch_bounds__(256) void k_encode_tiled(EncGemm g, int tiles_m, in
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-    const int nk = g.K / kEncBK;
-    const int fr = lane & 31, fk = 8 * (lane >> 5);
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) gload(kt + 1);
+    const int fr = lane & 31, fk = lane >> 5;      // fragment row; which half of 16 k
 #pragma unroll
-        for (int ks = 0; ks < kEncBK / 16; ++ks) {
+    for (int s = 0; s < NS - 1; ++s) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<(NS - 2) * (AL + BL)>();        // this wave's copies of stage kt landed
+        lds_barrier();                             // everyone's, and stage kt-1 is read
+        issue(kt + NS - 1);
+        const bf16* st = ring[kt % NS];
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
             bf16x8 af[WM], bfr[WN];
 #pragma unroll
-            for (int i = 0; i < WM; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(
-                    &As[buf][(wm + 32 * i + fr) * kEncLdk + 16 * ks + fk]);
+            for (int i = 0; i < WM; ++i) {
+                const int r = wm + 32 * i + fr;
+                af[i] = *reinterpret_cast<const bf16x8*>(st + r * BK +
+                                                         8 * ((2 * ks + fk) ^ enc_swz<SLOTS>(r)));
+            }
 #pragma unroll
-            for (int j = 0; j < WN; ++j)
-                bfr[j] = *reinterpret_cast<const bf16x8*>(
-                    &Bs[buf][(wn + 32 * j + fr) * kEncLdk + 16 * ks + fk]);
+            for (int j = 0; j < WN; ++j) {
+                const int r = BM + wn + 32 * j + fr;
+                bfr[j] = *reinterpret_cast<const bf16x8*>(st + r * BK +
+                                                          8 * ((2 * ks + fk) ^ enc_swz<SLOTS>(r)));
+            }
 #pragma unroll
             for (int i = 0; i < WM; ++i)
 #pragma unroll
                 for (int j = 0; j < WN; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
-        if (kt + 1 < nk) sstore(buf ^ 1);
-        __syncthreads();
     }
+    wait_vmcnt<0>();                               // no copy lands after the workgroup ends
 
     // lane l holds rows 8(v/4) + 4(l/32) + v%4, column l%32 of each 32x32 block
 #pragma unroll
@@ -227,15 +301,21 @@ static int launch_product(const EncGemm& g, int num_cus, hipStream_t st) {
         }
         return launch_status("query_encode");
     }
-    // the large tile when it alone fills every CU, else the small one
+    // the largest tile whose count still fills the CUs: 128x128, 128x64, else 64x64
     const int tm2 = (int)ceil_div(g.M, 128), tn2 = (int)ceil_div(g.N, 128);
+    const int tn1 = (int)ceil_div(g.N, 64), tm1 = (int)ceil_div(g.M, 64);
     if ((int64_t)tm2 * tn2 >= num_cus) {
         const unsigned grid = (unsigned)(8 * ceil_div((int64_t)tm2 * tn2, 8));
-        hipLaunchKernelGGL((k_encode_tiled<2, 2>), dim3(grid), dim3(256), 0, st, g, tm2, tn2);
+        hipLaunchKernelGGL((k_encode_tiled<2, 2, LSA_ENC_NS22, LSA_ENC_BK22>), dim3(grid), dim3(256), 0, st, g,
+                           tm2, tn2);
+    } else if ((int64_t)tm2 * tn1 * 100 >= (int64_t)LSA_ENC_FILL21 * num_cus) {
+        const unsigned grid = (unsigned)(8 * ceil_div((int64_t)tm2 * tn1, 8));
+        hipLaunchKernelGGL((k_encode_tiled<2, 1, LSA_ENC_NS21, LSA_ENC_BK21>), dim3(grid), dim3(256), 0, st, g,
+                           tm2, tn1);
     } else {
-        const int tm = (int)ceil_div(g.M, 64), tn = (int)ceil_div(g.N, 64);
-        const unsigned grid = (unsigned)(8 * ceil_div((int64_t)tm * tn, 8));
-        hipLaunchKernelGGL((k_encode_tiled<1, 1>), dim3(grid), dim3(256), 0, st, g, tm, tn);
+        const unsigned grid = (unsigned)(8 * ceil_div((int64_t)tm1 * tn1, 8));
+        hipLaunchKernelGGL((k_encode_tiled<1, 1, LSA_ENC_NS11, LSA_ENC_BK11>), dim3(grid), dim3(256), 0, st, g,
+                           tm1, tn1);
     }
     return launch_status("query_encode");
 }
@@ -265,6 +345,12 @@ extern "C" int lsa_query_encode(const void* h, int M, int d_model, int rank, int
                     rank);
     if ((int64_t)H * D > (1 << 20) || (int64_t)rank + H > (1 << 20) || d_model > (1 << 20))
         return fail(LSA_ERR_UNSUPPORTED, "lsa_query_encode: projection too large");
+    // the tiled product addresses every operand with 32-bit byte offsets
+    const int64_t lim = 0x7fffffff;
+    if ((int64_t)M * d_model * 2 > lim || (int64_t)M * rank * 2 > lim ||
+        (int64_t)rank * d_model * 2 > lim || (int64_t)H * D * rank * 2 > lim ||
+        (int64_t)H * d_model * 2 > lim)
+        return fail(LSA_ERR_UNSUPPORTED, "lsa_query_encode: an operand exceeds 2 GiB");
     int num_cus = 0;
     int rc = check_device(&num_cus);
     if (rc != LSA_OK) return rc;

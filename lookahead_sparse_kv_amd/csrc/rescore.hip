@@ -25,13 +25,6 @@ namespace lsa {
 
 constexpr int kRescoreRing = 4;          // LDS ring slots (groups of 16 rows) per wave
 constexpr int kRescoreGroupsPerWave = 32;
-constexpr int kRescoreWord3 = 0x00020000;   // raw buffer: 32-bit format, no swizzle/stride
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_rescore() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // MFMA operands as in the decode score kernel: lane l, n = l%16 picks the
 // candidate of the group, g = l/16 picks 8 of each 32 dims; A (queries) stays in
@@ -87,7 +80,7 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
 
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(keys + key_row_start[b] * D), (short)0, (int)min(S * D * 2, (int64_t)0x7fffffff),
-        kRescoreWord3);
+        kBufferWord3);
     // Group i goes to ring slot i % NB.  Copy j of a group moves rows RPI*j ..;
     // lane L fills physical slot L % SLOTS of row r = RPI*j + L/SLOTS.
     auto issue = [&](int i) {
@@ -129,13 +122,13 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
         // first use of Q, loaded after the first NB groups, waits for those)
         const int after = min(ngroups - 1, i + NB - 1) - i;
         if (after >= 3) {
-            wait_vmcnt_rescore<3 * DMAG>();
+            wait_vmcnt<3 * DMAG>();
         } else if (after == 2) {
-            wait_vmcnt_rescore<2 * DMAG>();
+            wait_vmcnt<2 * DMAG>();
         } else if (after == 1) {
-            wait_vmcnt_rescore<DMAG>();
+            wait_vmcnt<DMAG>();
         } else {
-            wait_vmcnt_rescore<0>();
+            wait_vmcnt<0>();
         }
         const bf16* slot = myring + (i % NB) * 16 * D + n16 * D;
         bf16x8 kb[KT];

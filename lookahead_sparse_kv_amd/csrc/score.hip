@@ -28,25 +28,6 @@ constexpr int kScoreRing = 4;          // LDS ring slots per wave (decode kernel
 constexpr int kNonTemporal = 2;
 constexpr int kScoreGroupsPerWave = 32;
 
-// Fourth word of a raw buffer resource (32-bit data format, no swizzle, no
-// stride), for buffer loads into LDS with byte offsets.
-constexpr int kBufferWord3Score = 0x00020000;
-
-// Workgroup barrier for LDS traffic only: this wave's LDS operations retire,
-// then s_barrier; outstanding global loads (copies of later data) stay in
-// flight across it.
-__device__ __forceinline__ void lds_barrier_score() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);    // lgkmcnt(0), vmcnt and expcnt left alone
-    __builtin_amdgcn_s_barrier();
-}
-
-// vmcnt(n) with the other counters left alone (n <= 63).  Stores count too, so
-// waiting on loads by this bound is conservative.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_score() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // ----------------------------------------------------------------- decode
 // One wave scores groups of 16 consecutive entries of one sequence.
@@ -133,10 +114,10 @@ __global__ __launch_bounds__(256) void k_score_decode(
         // (vector memory operations complete in issue order)
         const int after = min(ngroups - 1, i + NB - 1) - i;
         static_assert(NB <= 4, "waits below cover up to three later groups");
-        if (after >= 3) wait_vmcnt_score<3 * DMAG>();
-        else if (after == 2) wait_vmcnt_score<2 * DMAG>();
-        else if (after == 1) wait_vmcnt_score<DMAG>();
-        else wait_vmcnt_score<0>();
+        if (after >= 3) wait_vmcnt<3 * DMAG>();
+        else if (after == 2) wait_vmcnt<2 * DMAG>();
+        else if (after == 1) wait_vmcnt<DMAG>();
+        else wait_vmcnt<0>();
         const bf16* slot = myring + (i % NB) * 16 * D + n16 * D;
         bf16x8 kb[KT];
 #pragma unroll
@@ -239,7 +220,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
         for (int i = tid; i < NQ * QCHUNKS; i += 64 * NW) sq[i] = zero8();
         for (int i = tid; i < NQ * 64; i += 64 * NW) sw[i] = 0.0f;
     }
-    lds_barrier_score();
+    lds_barrier();
 
     // Copies of position t into ring slot t % NQ.  Lane L of query copy i of wave
     // wv fills LDS chunk p = (IPQ wv + i) 64 + L: head h = p / CH, physical chunk
@@ -251,7 +232,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
         const bool live = t < T;
         const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(q + ((int64_t)b * T + (live ? t : 0)) * H * D), (short)0,
-            live ? H * D * 2 : 0, kBufferWord3Score);
+            live ? H * D * 2 : 0, kBufferWord3);
 #pragma unroll
         for (int i = 0; i < IPQ; ++i) {
             const int p0 = (IPQ * wave + i) * 64;
@@ -264,7 +245,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
         }
         const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(w + ((int64_t)b * T + (live ? t : 0)) * H), (short)0, live ? H * 4 : 0,
-            kBufferWord3Score);
+            kBufferWord3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             wr, (__attribute__((address_space(3))) void*)(sw + slot * 64), 4, (uint32_t)(4 * lane), 0,
             0, 0);
@@ -278,8 +259,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
     for (int t = 0; t < NQ - 1; ++t) issue(t);
     for (int t = 0; t < T; ++t) {
         const int slot = t % NQ;
-        wait_vmcnt_score<(NQ - 2) * CPP>();   // position t landed (later ones may be in flight)
-        lds_barrier_score();                  // ... for every wave; all are done with t-1
+        wait_vmcnt<(NQ - 2) * CPP>();   // position t landed (later ones may be in flight)
+        lds_barrier();                  // ... for every wave; all are done with t-1
         issue(t + NQ - 1);                    // into t-1's slot
         const bf16x8* qs = sq + slot * QCHUNKS;
         // The two 32-head halves one after the other: half the accumulators live
@@ -325,7 +306,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
             }
         }
     }
-    wait_vmcnt_score<0>();                    // no copy lands after the workgroup ends
+    wait_vmcnt<0>();                    // no copy lands after the workgroup ends
     if (reduce_max && g == 0) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
