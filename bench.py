@@ -56,8 +56,11 @@ def parse():
 
 
 def src_sha(name: str) -> str:
-    p = os.path.join(REPO, "lookahead_sparse_kv_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of a kernel source and the device header it includes."""
+    h = hashlib.sha256()
+    for f in (name, "common.hpp"):
+        h.update(open(os.path.join(REPO, "lookahead_sparse_kv_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel: str, workload: str, src: str):
@@ -396,7 +399,8 @@ def main():
         "selected_fraction": round(float(counts.sum()) / float(wl.seq_len.sum()), 4),
         "roofline": roofline,
         "roofline_attend": roof_att,
-        "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s", None),
+        "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s",
+                                 read_traffic("rescore", args.workload, "rescore.hip")),
         "cpu_baseline": None,
     }
     t_e = enc["t"]
@@ -404,10 +408,12 @@ def main():
     line["kernels_us"]["query_encode_torch_mm"] = round(enc["t_lib"] * 1e6, 2)
     line["encoder"] = {"tokens": enc["M"], "d_model": enc["d_model"], "rank": enc["rank"],
                        "heads": wl.H, "head_dim": wl.D}
+    enc_traffic = read_traffic("encode", args.workload, "encode.hip")
     if enc["M"] <= 64:   # few tokens: a stream of the weights
-        line["roofline_encode"] = roof("hbm", enc["bytes"], t_e, HBM_PEAK_GBS, "GB/s", None)
+        line["roofline_encode"] = roof("hbm", enc["bytes"], t_e, HBM_PEAK_GBS, "GB/s", enc_traffic)
     else:
-        line["roofline_encode"] = roof("mfma", enc["flops"], t_e, BF16_PEAK_TFLOPS, "TFLOP/s", None)
+        line["roofline_encode"] = roof("mfma", enc["flops"], t_e, BF16_PEAK_TFLOPS, "TFLOP/s",
+                                       enc_traffic)
     line["decode_tokens_per_s_tau64_with_encoder"] = round(
         wl.B * wl.T / (t_attend + (t_e + t_score + t_select + t_topk) / 64.0), 1)
     if fetch is not None:
