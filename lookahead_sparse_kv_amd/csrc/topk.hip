@@ -75,6 +75,27 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Counts of four consecutive bins of COPIES lane-spread copies each (the
+// 16 COPIES bytes at `bins`, one thread's block).  A block is a whole number of
+// 128-byte bank rows and the threads' blocks are adjacent, so reading them in
+// the same order would put every lane of a 16-byte load on the same banks; lane
+// l starts at 16-byte chunk l instead and walks its block round robin.
+template <int COPIES>
+__device__ __forceinline__ void sum_bins4(const unsigned* bins, int lane, int (&c4)[4]) {
+    constexpr int CH = COPIES;                 // 16-byte chunks per block (4 bins x COPIES/4)
+    constexpr int CPB = COPIES / 4;            // chunks per bin
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c4[q] = 0;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+        const int c = (i + lane) & (CH - 1);
+        const u32x4 v = reinterpret_cast<const u32x4*>(bins)[c];
+        const int t = (int)(v[0] + v[1] + v[2] + v[3]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c4[q] += (c / CPB == q) ? t : 0;
+    }
+}
+
 // Search state: the need-th largest key among those with (key & pmask) == prefix
 // is the k-th key overall; m keys match; bits below hi are still open.
 struct RadixState {
@@ -96,6 +117,7 @@ __device__ void radix_refine(const uint32_t* keys, int n, RadixState& st, unsign
 __device__ __forceinline__ void digit_search(const unsigned* hist, int need, int* sh) {
     const int tid = threadIdx.x;
     int c4[4];
+    // (one wave; reading the blocks round robin as in the first digit measured slower here)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const u32x4* hq = reinterpret_cast<const u32x4*>(&hist[(4 * tid + q) * kHistCopies]);
@@ -203,12 +225,7 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
     {
         const int bb = 4 * (kTkThreads - 1 - tid);
         int c4[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const u32x4* hq = reinterpret_cast<const u32x4*>(&hist[(bb + q) * kCopies0]);
-            const u32x4 a = hq[0], c = hq[1];
-            c4[q] = (int)(a[0] + a[1] + a[2] + a[3] + c[0] + c[1] + c[2] + c[3]);
-        }
+        sum_bins4<kCopies0>(hist + bb * kCopies0, lane, c4);
         const int tot4 = c4[0] + c4[1] + c4[2] + c4[3];
         int total;
         const int above = block_excl_scan(tot4, scratch, &total);
@@ -311,11 +328,29 @@ __device__ void topk_regs(const float* __restrict__ rb, const int32_t* __restric
         scratch[kTkWaves + wave] = eq_w;
     }
     __syncthreads();
-    int pos = 0, eqs = 0;                                  // output slot and equal keys before this wave
-    for (int w2 = 0; w2 < wave; ++w2) {
-        const int e2 = scratch[kTkWaves + w2];
-        pos += scratch[w2] + max(0, min(need - eqs, e2));
-        eqs += e2;
+    // output slot and equal keys before this wave: lane j < 16 holds wave j's
+    // counts; one shuffle scan gives each wave's share of the equal keys
+    int pos, eqs;
+    {
+        const bool lw = lane < kTkWaves;
+        const int gtj = lw ? scratch[lane] : 0;
+        const int eqj = lw ? scratch[kTkWaves + lane] : 0;
+        int eq_incl = eqj;
+#pragma unroll
+        for (int off = 1; off < kTkWaves; off <<= 1) {
+            const int y = __shfl_up(eq_incl, off);
+            if (lane >= off) eq_incl += y;
+        }
+        const int eq_before = eq_incl - eqj;
+        int term = gtj + max(0, min(need - eq_before, eqj));   // wave j's selected keys
+#pragma unroll
+        for (int off = 1; off < kTkWaves; off <<= 1) {
+            const int y = __shfl_up(term, off);
+            if (lane >= off) term += y;
+        }
+        const int term_excl = __shfl(term, max(wave - 1, 0));
+        pos = wave > 0 ? term_excl : 0;
+        eqs = __shfl(eq_before, wave);
     }
 #pragma unroll
     for (int u = 0; u < RC; ++u) {
