@@ -23,7 +23,7 @@
 
 namespace lsa {
 
-constexpr int kRescoreRing = 4;          // LDS ring slots (groups of 16 rows) per wave
+constexpr int kRescoreRing = 3;          // LDS ring slots (groups of 16 rows) per wave
 constexpr int kRescoreGroupsPerWave = 32;
 
 // MFMA operands as in the decode score kernel: lane l, n = l%16 picks the
@@ -44,10 +44,13 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
     constexpr int NB = kRescoreRing;
     constexpr int GPW = kRescoreGroupsPerWave;
     static_assert(SLOTS >= 8 && NB <= 4, "layout");
-    // one LDS object: the rings, then the staged candidate indices
-    __shared__ __attribute__((aligned(16))) unsigned char lds[4 * NB * 16 * D * 2 + 4 * GPW * 16 * 4];
+    // one LDS object: the rings, the staged candidate indices, the queries
+    constexpr int OFF_IDX = 4 * NB * 16 * D * 2;
+    constexpr int OFF_Q = OFF_IDX + 4 * GPW * 16 * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[OFF_Q + 64 * D * 2];
     bf16* const myring = reinterpret_cast<bf16*>(lds) + (threadIdx.x >> 6) * (NB * 16 * D);
-    int* const myidx = reinterpret_cast<int*>(lds + 4 * NB * 16 * D * 2) + (threadIdx.x >> 6) * (GPW * 16);
+    int* const myidx = reinterpret_cast<int*>(lds + OFF_IDX) + (threadIdx.x >> 6) * (GPW * 16);
+    bf16* const sq = reinterpret_cast<bf16*>(lds + OFF_Q);    // [H][D] queries of the sequence
 
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
@@ -58,6 +61,15 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
     const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
     const int64_t nw = (int64_t)gridDim.x * 4;
     const int64_t G = (C + 15) / 16;
+    if ((int64_t)blockIdx.x * 4 >= G) return;    // no wave of this workgroup has a group
+    // The sequence's queries go to LDS once per workgroup (every wave needs all
+    // of them; a per-wave copy from memory would move as many bytes as the keys).
+    {
+        const bf16x8* qg = reinterpret_cast<const bf16x8*>(q + (int64_t)b * H * D);
+        for (int e = threadIdx.x; e < H * D / 8; e += 256)
+            reinterpret_cast<bf16x8*>(sq)[e] = qg[e];
+    }
+    __syncthreads();
     if (gw >= G) return;
     const int ngroups = (int)min((G - gw + nw - 1) / nw, (int64_t)GPW);
     const int n16 = lane & 15;
@@ -102,12 +114,12 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
 
     bf16x8 qa[MT][KT];
     float wv[MT][4];
-    const bf16* qb = q + (int64_t)b * H * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int head = min(16 * mt + n16, H - 1);
 #pragma unroll
-        for (int kk = 0; kk < KT; ++kk) qa[mt][kk] = load8(qb + (int64_t)head * D + 32 * kk + 8 * g);
+        for (int kk = 0; kk < KT; ++kk)
+            qa[mt][kk] = *reinterpret_cast<const bf16x8*>(sq + head * D + 32 * kk + 8 * g);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int hv = 16 * mt + 4 * g + v;
