@@ -527,8 +527,8 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
 // one 16-row query tile qt, two adjacent ones per thread; its threads issue
 // their loads of a batch of splits before the weights are formed, so the merge
 // costs about one memory round trip plus the bytes.
-template <int Dl, int SB>
-__global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit, int QG, int M,
+template <int Dl, int SB, int CT>
+__global__ __launch_bounds__(CT) void k_attend_combine(int n_blocks, int nsplit, int QG, int M,
                                                         const bf16* __restrict__ part_o,
                                                         const float* __restrict__ part_lse,
                                                         bf16* __restrict__ out,
@@ -537,10 +537,12 @@ __global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit
     constexpr int NDT = DPW / 16;
     constexpr int QT = kMQ / 16;
     constexpr int FPT = 4 * NDT * 64;           // fragments of one query tile (all u, nt, lanes)
-    constexpr int WPT = FPT / 512;              // workgroups per query tile (2 fragments a thread)
-    static_assert(FPT % 512 == 0, "fragment blocks");
+    constexpr int WPT = FPT / (2 * CT);         // workgroups per query tile (2 fragments a thread)
+    constexpr int NWV = CT / 64;                // waves
+    constexpr int JS = CT / 16;                 // split stride of the weight threads
+    static_assert(FPT % (2 * CT) == 0 && (CT == 128 || CT == 256), "fragment blocks");
     extern __shared__ float wsh[];              // [nsplit][16]: lse, then merge weights
-    __shared__ float red[4][16];
+    __shared__ float red[NWV][16];
     __shared__ float rinv[16];
 
     // Blocks are dealt to XCDs in contiguous ranges, as the attention kernel
@@ -560,7 +562,7 @@ __global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit
     // this thread's fragments: f and f+1, f = 2(part*256 + tid), over (u, nt,
     // lane) of tile qt -- adjacent lanes of one tile, so the same four rows and
     // latent dims d, d+1, one 16-byte load per split
-    const int f = 2 * (part * 256 + tid);
+    const int f = 2 * (part * CT + tid);
     const int lanef = f & 63;
     const int nt = (f >> 6) % NDT;
     const int u = (f >> 6) / NDT;
@@ -572,14 +574,14 @@ __global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit
 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     // Thread (r = tid % 16, j = tid / 16) forms the weights of row r for splits
-    // j, j+16, ...; the first LS of its lse values load before the partials, so
+    // j, j+JS, ...; the first LS of its lse values load before the partials, so
     // they do not queue behind them.
-    constexpr int LS = SB >= 32 ? 2 : 1;
+    constexpr int LS = SB / JS >= 2 ? SB / JS : 1;
     const float* pl = part_lse + ((int64_t)b * nsplit * QG + qg) * kMQ + 16 * qt;
     const int r = tid & 15, j = tid >> 4;
     float lsv[LS];
 #pragma unroll
-    for (int i = 0; i < LS; ++i) lsv[i] = pl[(int64_t)min(j + 16 * i, nsplit - 1) * QG * kMQ + r];
+    for (int i = 0; i < LS; ++i) lsv[i] = pl[(int64_t)min(j + JS * i, nsplit - 1) * QG * kMQ + r];
     __builtin_amdgcn_sched_barrier(0);          // the lse loads stay ahead of the partials
     // SB loads in flight, unconditional: indices past the last split repeat it
     // and get no weight
@@ -609,11 +611,11 @@ __global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < LS; ++i) {
-            const bool ok = j + 16 * i < nsplit;
+            const bool ok = j + JS * i < nsplit;
             mx = fmaxf(mx, ok ? lsv[i] : -INFINITY);
-            if (ok) wsh[(j + 16 * i) * 16 + r] = lsv[i];
+            if (ok) wsh[(j + JS * i) * 16 + r] = lsv[i];
         }
-        for (int s = j + 16 * LS; s < nsplit; s += 16) {
+        for (int s = j + JS * LS; s < nsplit; s += JS) {
             const float ls = pl[(int64_t)s * QG * kMQ + r];
             wsh[s * 16 + r] = ls;
             mx = fmaxf(mx, ls);
@@ -622,9 +624,11 @@ __global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         if (lane < 16) red[wave][r] = mx;
         lds_barrier();
-        mx = fmaxf(fmaxf(red[0][r], red[1][r]), fmaxf(red[2][r], red[3][r]));
+        mx = red[0][r];
+#pragma unroll
+        for (int wv = 1; wv < NWV; ++wv) mx = fmaxf(mx, red[wv][r]);
         float tot = 0.0f;
-        for (int s = j; s < nsplit; s += 16) {
+        for (int s = j; s < nsplit; s += JS) {
             const float ls = wsh[s * 16 + r];
             const float w = ls == -INFINITY ? 0.0f : expf(ls - mx);
             wsh[s * 16 + r] = w;
@@ -636,7 +640,8 @@ __global__ __launch_bounds__(256) void k_attend_combine(int n_blocks, int nsplit
         if (lane < 16) red[wave][r] = tot;
         lds_barrier();
         if (tid < 16) {
-            tot = (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
+            tot = NWV == 4 ? (red[0][r] + red[1][r]) + (red[2][r] + red[NWV - 1][r])
+                           : red[0][r] + red[NWV - 1][r];
             rinv[r] = tot > 0.0f ? 1.0f / tot : 0.0f;
             const int ql = 16 * qt + r;
             if (lse && part == 0 && qg * kMQ + ql < M)
@@ -798,7 +803,8 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(LSA_ERR_WORKSPACE, "lsa_sparse_attend: workspace %zu < %zu bytes",
                     workspace_bytes, need);
-    int rc = check_device(nullptr);
+    int cus = 0;
+    int rc = check_device(&cus);
     if (rc != LSA_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
 
@@ -826,20 +832,28 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
         rc = launch_status("attend_mfma");
         if (rc != LSA_OK || p.nsplit == 1) return rc;
         // partials: one [kMQ x Dl] block per (b, split, query group)
-        const int cblocks = B * p.QG * (kMQ / 16) * (Dl / 128);
+        // 256-thread blocks, or 128-thread ones (twice as many) when the 256-thread
+        // grid would leave CUs idle: every thread keeps all SB loads in flight, so
+        // the rate follows the number of CUs holding blocks
+        const int blocks256 = B * p.QG * (kMQ / 16) * (Dl / 128);
+        const bool small_blocks = blocks256 < cus;
+        const int cblocks = small_blocks ? 2 * blocks256 : blocks256;
         const unsigned cgrid = (unsigned)(8 * ((cblocks + 7) / 8));
         const size_t cshm = sizeof(float) * 16 * (size_t)p.nsplit;
+#define LSA_COMB_CT(dl, sb, ct)                                                                \
+    hipLaunchKernelGGL((k_attend_combine<dl, sb, ct>), dim3(cgrid), dim3(ct), cshm, st, cblocks,  \
+                       p.nsplit, p.QG, M, part_o, part_lse, (bf16*)out, lse)
 #define LSA_COMB(dl, sb)                                                                       \
-    hipLaunchKernelGGL((k_attend_combine<dl, sb>), dim3(cgrid), dim3(256), cshm, st, cblocks,     \
-                       p.nsplit,                                                               \
-                       p.QG, M, part_o, part_lse, (bf16*)out, lse)
+    if (small_blocks) LSA_COMB_CT(dl, sb, 128); else LSA_COMB_CT(dl, sb, 256)
 #define LSA_COMB_DL(sb)                                                                        \
-    if (Dl == 512) LSA_COMB(512, sb); else if (Dl == 256) LSA_COMB(256, sb); else LSA_COMB(128, sb)
+    if (Dl == 512) { LSA_COMB(512, sb); } else if (Dl == 256) { LSA_COMB(256, sb); }           \
+    else { LSA_COMB(128, sb); }
         if (p.nsplit <= 8) { LSA_COMB_DL(8); }
         else if (p.nsplit <= 16) { LSA_COMB_DL(16); }
         else { LSA_COMB_DL(32); }
 #undef LSA_COMB_DL
 #undef LSA_COMB
+#undef LSA_COMB_CT
         return launch_status("attend_combine");
     }
     const unsigned blocks = (unsigned)((int64_t)B * T * Hq);
