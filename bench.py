@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode_500k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=4, help="sequences the CPU baseline scores")
+    ap.add_argument("--cpu-seqs", type=int, default=8, help="sequences the CPU baseline scores")
     ap.add_argument("--kernel-reps", type=int, default=0,
                     help="launches per timing interval (0 = pick for >= 1 ms)")
     ap.add_argument("--fetch-reps", type=int, default=4,
