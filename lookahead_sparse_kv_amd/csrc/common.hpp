@@ -42,6 +42,15 @@ __device__ __forceinline__ bf16x8 zero8() {
 
 __device__ __forceinline__ float sigmoidf(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// max(x, 0) in one integer instruction: an fp32 value with its sign bit clear
+// is a non-negative int32, one with it set (-0.0 included) a negative one, so
+// max_i32(bits, 0) returns x for x >= +0.0 and +0.0 otherwise (a NaN keeps its
+// bits).  fmaxf(x, 0.0f) costs two instructions on a matrix-core result, which
+// the compiler first canonicalises.
+__device__ __forceinline__ float relu_bits(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Word 3 of a buffer resource for plain raw buffer loads on gfx950; a load
 // past num_records (or through a range of 0) reads no memory.
 constexpr int kBufferWord3 = 0x00020000;

@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
+            for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * relu_bits(acc[mt][v]);
         sacc += __shfl_xor(sacc, 16);
         sacc += __shfl_xor(sacc, 32);
         const int64_t p = 16 * (gw + nw * (int64_t)i) + n16;

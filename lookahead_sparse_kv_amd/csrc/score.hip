@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_score_decode(
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * fmaxf(acc[mt][v], 0.0f);
+            for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * relu_bits(acc[mt][v]);
         sacc += __shfl_xor(sacc, 16);
         sacc += __shfl_xor(sacc, 32);
         const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) s[nt] += wq[v] * fmaxf(acc[nt][4 * j + v], 0.0f);
+                    for (int v = 0; v < 4; ++v) s[nt] += wq[v] * relu_bits(acc[nt][4 * j + v]);
             }
         }
 #pragma unroll
