@@ -89,26 +89,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select_scatter(
 
     __shared__ int wsum[kSelThreads / kWave];
     __shared__ int base_sh;
+    // The tile's logits load first, so they are in flight with the counts of the
+    // tiles before it (the barriers below wait for LDS only, not for them).
+    const int64_t s0 = (int64_t)tile * kTile + (int64_t)threadIdx.x * kSelPer;
+    float v[kSelPer];
+    const bool live = (int64_t)tile * kTile < S;
+    if (live) load_tile8(z + entry_start[b], s0, S, v);
     // offset of this tile = counts of the tiles before it
     int pre = 0;
     for (int i = threadIdx.x; i < tile; i += kSelThreads) pre += tile_count[(int64_t)b * ntiles + i];
     for (int off = 32; off > 0; off >>= 1) pre += __shfl_xor(pre, off);
     if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = pre;
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) {
         int t = 0;
         for (int i = 0; i < kSelThreads / kWave; ++i) t += wsum[i];
         base_sh = t;
     }
-    __syncthreads();
+    lds_barrier();
     const int base = base_sh;
 
-    const int64_t s0 = (int64_t)tile * kTile + (int64_t)threadIdx.x * kSelPer;
-    float v[kSelPer];
     bool keep[kSelPer];
     int c = 0;
-    if ((int64_t)tile * kTile < S) {
-        load_tile8(z + entry_start[b], s0, S, v);
+    if (live) {
 #pragma unroll
         for (int j = 0; j < kSelPer; ++j) {
             keep[j] = s0 + j < S && gate(v[j], thr);
@@ -119,9 +122,9 @@ __global__ __launch_bounds__(kSelThreads) void k_select_scatter(
         for (int j = 0; j < kSelPer; ++j) keep[j] = false;
     }
     const int incl = wave_incl_scan(c);
-    __syncthreads();  // wsum reuse
+    lds_barrier();  // wsum reuse
     if ((threadIdx.x & 63) == 63) wsum[threadIdx.x >> 6] = incl;
-    __syncthreads();
+    lds_barrier();
     int wpre = 0;
     const int w = threadIdx.x >> 6;
     for (int i = 0; i < w; ++i) wpre += wsum[i];
