@@ -140,6 +140,34 @@ def _layers(seed, B, T, H, D, lens, n_layers, dtype="bf16"):
                                 bias=-2.0 + 0.5 * l) for l in range(n_layers)]
 
 
+def test_union_over_indexers_long_lists(ref):
+    """Sequences long enough that every wave of the decode kernel streams more
+    groups than its ring holds (so ring slots and their prefetched union values
+    are reused); the reference scores sampled entries of each indexer."""
+    layers = _layers(91, 2, 1, 64, 128, [60000, 45000], 3)
+    z = torch.full((layers[0].total_entries,), float("nan"), device="cuda")
+    for i, wl in enumerate(layers):
+        announce(f"union over long lists, layer {i}")
+        lsa.lsa_index_score(dev(wl.keys), dev(wl.key_row_start), dev(wl.seq_len),
+                            dev(wl.entry_start), wl.max_len, dev(wl.q), dev(wl.w), wl.bias,
+                            1 if i == 0 else 2, z)
+    torch.cuda.synchronize()
+    zg = host(z).astype(np.float64)
+    rng = np.random.default_rng(92)
+    wl0 = layers[0]
+    for b in range(wl0.B):
+        S, es = int(wl0.seq_len[b]), int(wl0.entry_start[b])
+        s = np.sort(rng.choice(S, size=1500, replace=False))
+        zr = None
+        for wl in layers:
+            rows = wl.keys[int(wl.key_row_start[b]) + s]
+            zl, _ = ref.index_score(rows, np.zeros(1, np.int64), np.array([len(s)], np.int32),
+                                    np.zeros(1, np.int64), wl.q[b:b + 1], wl.w[b:b + 1], wl.bias,
+                                    reduce_max=True, want_prob=False)
+            zr = zl if zr is None else np.maximum(zr, zl)
+        check_scores(zg[es + s], zr)
+
+
 @pytest.mark.parametrize("T,H,D,lens,dtype", [
     (1, 64, 128, [3000, 1, 777], "bf16"),     # decode kernel
     (4, 64, 128, [513, 300], "bf16"),          # burst kernel
