@@ -235,6 +235,9 @@ def main():
                 p.step(i)
             for i in range(args.profile_launches):
                 p.rescore(i)
+            if wl.T == 1:
+                for i in range(args.profile_launches):
+                    p.score_union(3, i)
             enc_call = encoder_setup(torch, lsa, inputs, wl, rotate=False)[0]
             for i in range(args.profile_launches):
                 enc_call(i)
@@ -287,9 +290,12 @@ def main():
         t_rescore = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.rescore(i) for i in range(r)]), r)
         t_topk_native = timed_graph(torch, stream, capture(torch, stream, [p.topk_native] * r), r)
-        # OR-mode union of three indexers (three score launches, the last two combining)
+        # OR-mode union of three indexers: three score launches (the last two
+        # combining), and the single streaming launch
         r = max(2, reps_for(step_s) // 3)
         t_union3 = timed_graph(torch, stream, capture(
+            torch, stream, [lambda i=i: p.score_union(3, 3 * i, fused=False) for i in range(r)]), r)
+        t_union3f = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.score_union(3, 3 * i) for i in range(r)]), r)
         # Memory-Indexer query encoder: the step's B*T hidden states -> q, w (weight
         # replicas rotate, as a trigger finds them in HBM); beside it, the same two
@@ -345,6 +351,8 @@ def main():
         score_bytes = int(wl.seq_len.sum()) * wl.D * 2
     score_bytes += wl.q.nbytes + wl.w.nbytes + int(wl.seq_len.sum()) * 4
     score_flops = 2.0 * scores_per_step * wl.H * wl.D
+    # union of three indexers in one launch: three key sets, queries and gates, one logit write
+    union3_bytes = 3 * (score_bytes - int(wl.seq_len.sum()) * 4) + int(wl.seq_len.sum()) * 4
     att_alg_bytes = att_bytes + wl.qa.nbytes * 2 + wl.B * wl.k * 4   # rows, qa in, out, indices
     att_flops = 4.0 * wl.B * wl.T * wl.Hq * (wl.k + wl.max_hca) * wl.Dl
     # native re-score: per candidate one key row, its index and its logit; the queries
@@ -389,7 +397,8 @@ def main():
                        "sparse_attend": round(t_attend * 1e6, 2),
                        "index_rescore": round(t_rescore * 1e6, 2),
                        "topk_native": round(t_topk_native * 1e6, 2),
-                       "index_score_union3": round(t_union3 * 1e6, 2)},
+                       "index_score_union3": round(t_union3 * 1e6, 2),
+                       "index_score_union3_fused": round(t_union3f * 1e6, 2)},
         "index_scores_per_s": round(scores_per_step / t_score, 1),
         "decode_tokens_per_s": round(wl.B * wl.T / t_attend, 1),
         "decode_tokens_per_s_tau64": round(
@@ -401,6 +410,9 @@ def main():
         "roofline_attend": roof_att,
         "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s",
                                  read_traffic("rescore", args.workload, "rescore.hip")),
+        "roofline_union3": None if wl.T != 1 else roof(
+            "hbm", union3_bytes, t_union3f, HBM_PEAK_GBS, "GB/s",
+            read_traffic("score_union", args.workload, "score.hip")),
         "cpu_baseline": None,
     }
     t_e = enc["t"]

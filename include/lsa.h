@@ -106,6 +106,28 @@ int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
                     int D, int64_t max_len, const void* q, const float* w, float bias,
                     int reduce_max, float* z_out, float* prob_out, void* stream);
 
+/* OR-union of several indexers' scores in one call (section 2.4
+ * "Multi-Layer Indexers": a context entry is kept when the gate of any of the
+ * indexers keeps it, and as sigmoid is monotone that is the gate on the
+ * largest logit).  For l = 0 .. n_idx-1, indexer l has its own keys[l],
+ * q[l], w[l] and bias[l], laid out as for lsa_index_score; all share the
+ * sequence layout (key_row_start, seq_len, entry_start), dtype, B, T, H, D.
+ *   z_out[entry_start[b] + s] = max over l and t of z_l[b,t,s];
+ *   prob_out, if not NULL, holds its sigmoid.
+ * keys, q, w and bias are HOST arrays of n_idx entries; the pointers in
+ * keys, q and w are device pointers.  The bf16 matrix-core shapes with T = 1
+ * (H <= 64, D in {64, 128}) stream every indexer's keys in one launch and
+ * keep the running maximum in registers, so z_out is written once; the
+ * result is bit-identical to calling lsa_index_score once per indexer
+ * (reduce_max = 1, then 2).  Other shapes make exactly those calls.
+ * Envelope: 1 <= n_idx <= 4; otherwise as lsa_index_score.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int lsa_index_score_union(int n_idx, const void* const* keys, int dtype,
+                          const int64_t* key_row_start, const int32_t* seq_len,
+                          const int64_t* entry_start, int B, int T, int H, int D,
+                          int64_t max_len, const void* const* q, const float* const* w,
+                          const float* bias, float* z_out, float* prob_out, void* stream);
+
 /* Native re-score of the kept subset (section 2.1 "Tiered Selection": the
  * backbone's native Lightning Indexer takes the fine-grained top-k inside the
  * fetched subset; section 2.3 "Decoupled Training": the compressed indexer

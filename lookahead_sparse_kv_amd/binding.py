@@ -27,8 +27,8 @@ LSA_OP_SELECT = 1
 LSA_OP_TOPK = 2
 LSA_OP_ATTEND = 3
 
-EXPORTED = ["lsa_query_encode", "lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
-            "lsa_fetch_rows",
+EXPORTED = ["lsa_query_encode", "lsa_index_score", "lsa_index_score_union", "lsa_index_rescore",
+            "lsa_select_compact", "lsa_topk", "lsa_fetch_rows",
             "lsa_sparse_attend",
             "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
 
@@ -54,6 +54,7 @@ def load_library(path: str = LIB_PATH):
     P, I, L, F, Z = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                      ctypes.c_size_t)
     lib.lsa_index_score.argtypes = [P, I, P, P, P, I, I, I, I, L, P, P, F, I, P, P, P]
+    lib.lsa_index_score_union.argtypes = [I, P, I, P, P, P, I, I, I, I, L, P, P, P, P, P, P]
     lib.lsa_index_rescore.argtypes = [P, I, P, P, P, P, P, I, I, I, L, P, P, P, P]
     lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
     lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, I, P, Z, P]
@@ -142,6 +143,41 @@ def lsa_index_score(keys, key_row_start, seq_len, entry_start, max_len: int, q, 
                              float(bias), int(reduce_max), _ptr(z_out), _ptr(prob_out),
                              _stream(stream))
     _check("lsa_index_score", rc)
+    return z_out, prob_out
+
+
+def lsa_index_score_union(keys, key_row_start, seq_len, entry_start, max_len: int, qs, ws,
+                          biases, z_out, prob_out=None, stream=None):
+    """OR-union over indexers (see include/lsa.h): keys, qs, ws and biases are
+    sequences with one entry per indexer; q: [B, T, H, D], w: [B, T, H]."""
+    lib = load_library()
+    n = len(keys)
+    if not (len(qs) == len(ws) == len(biases) == n):
+        raise ValueError("keys, qs, ws and biases need one entry per indexer")
+    B, T, H, D = qs[0].shape
+    for k, q, w in zip(keys, qs, ws):
+        _dev(k, "keys", keys[0].dtype)
+        _dev(q, "q", keys[0].dtype)
+        _dev(w, "w", torch.float32)
+        if tuple(q.shape) != (B, T, H, D) or tuple(w.shape) != (B, T, H):
+            raise ValueError("every indexer needs q [B, T, H, D] and w [B, T, H] of one shape")
+        if k.dim() != 2 or k.shape[1] != D:
+            raise ValueError("keys must be [rows, D]")
+    _dev(key_row_start, "key_row_start", torch.int64)
+    _dev(seq_len, "seq_len", torch.int32)
+    _dev(entry_start, "entry_start", torch.int64)
+    _dev(z_out, "z_out", torch.float32)
+    if prob_out is not None:
+        _dev(prob_out, "prob_out", torch.float32)
+    arr = ctypes.c_void_p * n
+    kp = arr(*(k.data_ptr() for k in keys))
+    qp = arr(*(q.data_ptr() for q in qs))
+    wp = arr(*(w.data_ptr() for w in ws))
+    bp = (ctypes.c_float * n)(*(float(b) for b in biases))
+    rc = lib.lsa_index_score_union(n, kp, _dtype_code(keys[0]), _ptr(key_row_start),
+                                   _ptr(seq_len), _ptr(entry_start), B, T, H, D, int(max_len), qp,
+                                   wp, bp, _ptr(z_out), _ptr(prob_out), _stream(stream))
+    _check("lsa_index_score_union", rc)
     return z_out, prob_out
 
 

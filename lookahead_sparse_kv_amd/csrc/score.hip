@@ -149,6 +149,182 @@ __global__ __launch_bounds__(256) void k_score_decode(
     }
 }
 
+// ------------------------------------------------------------ fused union
+// OR-mode union of up to kUnionMax indexers in one pass (T = 1): the decode
+// kernel's streaming with (indexer, group) as the unit.  A wave takes its
+// groups for indexer 0, then the same groups for indexer 1, ... ; the ring runs
+// on across the switch (the copies of the next indexer's first groups are in
+// flight while the last groups of the current one are scored), and the queries
+// and weights of the next indexer load into registers at the switch.  The
+// running maximum of the wave's <= kScoreGroupsPerWave groups stays in
+// registers, spread over lanes (lane 16 j + n of zmax[s] holds entry n of group
+// 4 s + j, which the head-sum shuffles leave in that lane), and is written
+// once at the end.  Each entry's logit is computed as in the decode kernel, so
+// the union is bit-identical to the one the combining launches produce.
+constexpr int kUnionMax = 4;
+struct UnionArgs {
+    const bf16* keys[kUnionMax];
+    const bf16* q[kUnionMax];
+    const float* w[kUnionMax];
+    float bias[kUnionMax];
+    int n;
+};
+
+// u.x[l] for a wave-uniform l, kept in scalar registers: each argument passes
+// through readfirstlane before the selection, so the choice cannot turn back
+// into an indexed (vector) load of the argument block
+__device__ __forceinline__ uint32_t sgpr32(uint32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ T* sgpr_ptr(T* p) {
+    const uint64_t x = (uint64_t)p;
+    return (T*)(((uint64_t)sgpr32((uint32_t)(x >> 32)) << 32) | sgpr32((uint32_t)x));
+}
+template <typename T>
+__device__ __forceinline__ T* pick(T* const (&a)[kUnionMax], int l) {
+    l = (int)sgpr32((uint32_t)l);
+    T* r = sgpr_ptr(a[0]);
+#pragma unroll
+    for (int j = 1; j < kUnionMax; ++j)
+        if (l == j) r = sgpr_ptr(a[j]);
+    return r;
+}
+__device__ __forceinline__ float pick(const float (&a)[kUnionMax], int l) {
+    l = (int)sgpr32((uint32_t)l);
+    float r = __uint_as_float(sgpr32(__float_as_uint(a[0])));
+#pragma unroll
+    for (int j = 1; j < kUnionMax; ++j)
+        if (l == j) r = __uint_as_float(sgpr32(__float_as_uint(a[j])));
+    return r;
+}
+
+template <int MT, int KT>
+__global__ __launch_bounds__(256) void k_score_union(
+    UnionArgs u, const int64_t* __restrict__ key_row_start, const int32_t* __restrict__ seq_len,
+    const int64_t* __restrict__ entry_start, int H, int64_t max_len, float* __restrict__ z_out,
+    float* __restrict__ prob_out) {
+    constexpr int D = 32 * KT;
+    constexpr int SLOTS = D / 8;
+    constexpr int RPI = 64 / SLOTS;
+    constexpr int DMAG = 16 / RPI;
+    constexpr int NB = kScoreRing;
+    constexpr int ZS = kScoreGroupsPerWave / 4;    // running-max registers per lane
+    static_assert(SLOTS >= 16 || SLOTS == 8, "row layout");
+    static_assert((NB & (NB - 1)) == 0, "ring slots: a power of two");
+    __shared__ __attribute__((aligned(16))) bf16 ring[4][NB][16 * D];
+
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t S = min((int64_t)seq_len[b], max_len);
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    const int64_t G = (S + 15) / 16;
+    if (gw >= G) return;
+    // at most kScoreGroupsPerWave by the launch's grid
+    const int ngroups = (int)min((G - gw + nw - 1) / nw, (int64_t)kScoreGroupsPerWave);
+    const int nunits = ngroups * u.n;
+    const int64_t last = S;
+    const int n16 = lane & 15;
+    const int g = lane >> 4;
+    const int64_t krs = key_row_start[b];
+    const int64_t eo = entry_start[b];
+    bf16* myring = &ring[wave][0][0];
+
+    // the next unit to copy: number vn, indexer il, group ii of this wave
+    int vn = 0, il = 0, ii = 0;
+    auto issue_next = [&]() {
+        const bf16* kbase = pick(u.keys, il) + krs * D;
+        const int64_t e0 = 16 * (gw + nw * (int64_t)ii);
+        bf16* slot = myring + (vn & (NB - 1)) * 16 * D;
+#pragma unroll
+        for (int j = 0; j < DMAG; ++j) {
+            const int r = RPI * j + lane / SLOTS;
+            const int64_t e = min(e0 + r, last - 1);
+            const int ps = lane % SLOTS;
+            const bf16* src = kbase + e * D + 8 * (ps ^ (r & (SLOTS - 1) & 15));
+            __builtin_amdgcn_global_load_lds(
+                (const void*)src, (__attribute__((address_space(3))) void*)(slot + RPI * j * D),
+                16, 0, kNonTemporal);
+        }
+        ++vn;
+        if (++ii == ngroups) { ii = 0; ++il; }
+    };
+#pragma unroll
+    for (int v = 0; v < NB; ++v)
+        if (vn < nunits) issue_next();
+
+    float zmax[ZS];
+#pragma unroll
+    for (int s8 = 0; s8 < ZS; ++s8) zmax[s8] = -INFINITY;
+    const int rsw = n16 & (SLOTS - 1) & 15;
+    int v = 0;                                     // unit being scored
+    for (int l = 0; l < u.n; ++l) {
+        bf16x8 qa[MT][KT];
+        float wv[MT][4];
+        const bf16* qb = pick(u.q, l) + (int64_t)b * H * D;
+        const float* wb = pick(u.w, l) + (int64_t)b * H;
+        const float bias = pick(u.bias, l);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int head = min(16 * mt + n16, H - 1);
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk)
+                qa[mt][kk] = load8(qb + (int64_t)head * D + 32 * kk + 8 * g);
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int hv = 16 * mt + 4 * g + q4;
+                wv[mt][q4] = hv < H ? wb[hv] : 0.0f;
+            }
+        }
+        // queries and weights in registers (the ring's copies in flight retire too:
+        // vector memory operations complete in issue order)
+        wait_vmcnt<0>();
+        for (int i = 0; i < ngroups; ++i, ++v) {
+            // unit v's copies landed (later units' copies may stay in flight)
+            const int after = min(nunits - 1, v + NB - 1) - v;
+            static_assert(NB <= 4, "waits below cover up to three later units");
+            if (after >= 3) wait_vmcnt<3 * DMAG>();
+            else if (after == 2) wait_vmcnt<2 * DMAG>();
+            else if (after == 1) wait_vmcnt<DMAG>();
+            else wait_vmcnt<0>();
+            const bf16* slot = myring + (v & (NB - 1)) * 16 * D + n16 * D;
+            bf16x8 kb[KT];
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk)
+                kb[kk] = *reinterpret_cast<const bf16x8*>(slot + 8 * ((4 * kk + g) ^ rsw));
+            f32x4 acc[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KT; ++kk)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(qa[mt][kk], kb[kk], acc[mt]);
+            if (vn < nunits) issue_next();
+            float sacc = 0.0f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) sacc += wv[mt][q4] * relu_bits(acc[mt][q4]);
+            sacc += __shfl_xor(sacc, 16);
+            sacc += __shfl_xor(sacc, 32);
+            const float z = sacc + bias;
+            // every lane holds entry n16's logit; lane 16 (i % 4) + n16 keeps it
+#pragma unroll
+            for (int s8 = 0; s8 < ZS; ++s8)
+                if ((i >> 2) == s8 && (i & 3) == g) zmax[s8] = fmaxf(zmax[s8], z);
+        }
+    }
+#pragma unroll
+    for (int s8 = 0; s8 < ZS; ++s8) {
+        const int i = 4 * s8 + g;
+        const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
+        if (i < ngroups && n < last) {
+            z_out[eo + n] = zmax[s8];
+            if (prob_out) prob_out[eo + n] = sigmoidf(zmax[s8]);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ burst
 // Workgroup = 4 waves x 64 entries of one sequence; it walks all T positions.
 // Keys of the wave's 64 entries stay in registers as B operands (32x32x16,
@@ -464,4 +640,76 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
                            key_row_start, seq_len, entry_start, T, H, D, max_len, (const bf16*)q,
                            w, bias, reduce_max, z_out, prob_out);
     return launch_status("score_vector");
+}
+
+extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dtype,
+                                     const int64_t* key_row_start, const int32_t* seq_len,
+                                     const int64_t* entry_start, int B, int T, int H, int D,
+                                     int64_t max_len, const void* const* q,
+                                     const float* const* w, const float* bias, float* z_out,
+                                     float* prob_out, void* stream) {
+    clear_error();
+    if (!keys || !q || !w || !bias)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: a required array is NULL");
+    if (n_idx < 1 || n_idx > kUnionMax)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: n_idx=%d not in 1..%d", n_idx,
+                    kUnionMax);
+    for (int l = 0; l < n_idx; ++l)
+        if (!keys[l] || !q[l] || !w[l])
+            return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: indexer %d has a NULL pointer",
+                        l);
+    const bool fused = dtype == LSA_DTYPE_BF16 && T == 1 && H <= 64 && (D == 64 || D == 128);
+    if (!fused) {
+        // other shapes: one score launch per indexer, each combining with the last
+        for (int l = 0; l < n_idx; ++l) {
+            const int rc = lsa_index_score(keys[l], dtype, key_row_start, seq_len, entry_start, B,
+                                           T, H, D, max_len, q[l], w[l], bias[l],
+                                           l == 0 ? 1 : 2, z_out,
+                                           l == n_idx - 1 ? prob_out : nullptr, stream);
+            if (rc != LSA_OK) return rc;
+        }
+        return LSA_OK;
+    }
+    // the same validation as one score call, per indexer
+    for (int l = 0; l < n_idx; ++l) {
+        if (!aligned16(keys[l]) || !aligned16(q[l]))
+            return fail(LSA_ERR_INVALID_ARG,
+                        "lsa_index_score_union: keys and q of indexer %d must be 16-byte aligned", l);
+    }
+    if (!key_row_start || !seq_len || !entry_start || !z_out)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: a required pointer is NULL");
+    if (B <= 0 || H <= 0 || max_len < 0)
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: B=%d H=%d max_len=%lld", B, H,
+                    (long long)max_len);
+    if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "lsa_index_score_union: B=%d > 65535", B);
+    if (max_len > (int64_t)1 << 31)
+        return fail(LSA_ERR_UNSUPPORTED, "lsa_index_score_union: max_len too large");
+    int cus = 0;
+    int rc = check_device(&cus);
+    if (rc != LSA_OK) return rc;
+    if (max_len == 0) return LSA_OK;
+    UnionArgs ua{};
+    for (int l = 0; l < n_idx; ++l) {
+        ua.keys[l] = (const bf16*)keys[l];
+        ua.q[l] = (const bf16*)q[l];
+        ua.w[l] = w[l];
+        ua.bias[l] = bias[l];
+    }
+    ua.n = n_idx;
+    const int64_t groups = ceil_div(max_len, 16);
+    int64_t gpw = (groups * B) / ((int64_t)cus * 4);
+    gpw = gpw < 1 ? 1 : (gpw > kScoreGroupsPerWave ? kScoreGroupsPerWave : gpw);
+    dim3 grid((unsigned)ceil_div(groups, gpw * 4), (unsigned)B);
+    const int MT = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
+    hipStream_t st = (hipStream_t)stream;
+#define LSA_UNI(mt, kt)                                                                       \
+    hipLaunchKernelGGL((k_score_union<mt, kt>), grid, dim3(256), 0, st, ua, key_row_start,     \
+                       seq_len, entry_start, H, max_len, z_out, prob_out)
+    if (D == 128) {
+        if (MT == 1) LSA_UNI(1, 4); else if (MT == 2) LSA_UNI(2, 4); else LSA_UNI(4, 4);
+    } else {
+        if (MT == 1) LSA_UNI(1, 2); else if (MT == 2) LSA_UNI(2, 2); else LSA_UNI(4, 2);
+    }
+#undef LSA_UNI
+    return launch_status("score_union");
 }

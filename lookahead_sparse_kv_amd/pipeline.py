@@ -102,12 +102,19 @@ class Pipeline:
                             d.entry_start, d.max_len, d.q, d.w, d.bias, reduce_max=True,
                             z_out=self.z, prob_out=self.prob, stream=stream)
 
-    def score_union(self, n_indexers: int, replica: int = 0, stream=None):
+    def score_union(self, n_indexers: int, replica: int = 0, fused: bool = True, stream=None):
         """OR-mode union of n indexers (key replicas replica .. replica+n-1 stand in
-        for the indexers' key sets), gate logits left in z."""
+        for the indexers' key sets), gate logits left in z: one lsa_index_score_union
+        call, or (fused=False) one lsa_index_score call per indexer."""
         d = self.d
+        keys = [d.keys[(replica + i) % len(d.keys)] for i in range(n_indexers)]
+        if fused:
+            lsa.lsa_index_score_union(keys, d.key_row_start, d.seq_len, d.entry_start, d.max_len,
+                                      [d.q] * n_indexers, [d.w] * n_indexers,
+                                      [d.bias] * n_indexers, self.z, stream=stream)
+            return
         for i in range(n_indexers):
-            lsa.lsa_index_score(d.keys[(replica + i) % len(d.keys)], d.key_row_start, d.seq_len,
+            lsa.lsa_index_score(keys[i], d.key_row_start, d.seq_len,
                                 d.entry_start, d.max_len, d.q, d.w, d.bias,
                                 reduce_max=1 if i == 0 else 2, z_out=self.z, stream=stream)
 

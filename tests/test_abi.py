@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_calls():
     syms = declared_symbols()
-    for s in ("lsa_query_encode", "lsa_index_score", "lsa_index_rescore", "lsa_select_compact",
+    for s in ("lsa_query_encode", "lsa_index_score", "lsa_index_score_union", "lsa_index_rescore", "lsa_select_compact",
               "lsa_topk", "lsa_fetch_rows", "lsa_sparse_attend", "lsa_workspace_bytes",
               "lsa_status_string", "lsa_last_error", "lsa_version"):
         assert s in syms
@@ -200,3 +200,32 @@ def test_rescore_validation(lib):
     assert f(*a) == -2
     a = list(args); a[1] = 0; a[8] = 200; a[9] = 200  # fp32 vector path too large
     assert f(*a) == -2
+
+
+def test_score_union_validation(lib):
+    P = FAKE
+    f = lib.lsa_index_score_union
+    arr = ctypes.c_void_p * 4
+    ks, qs, ws = arr(P, P, P, P), arr(P, P, P, P), arr(P, P, P, P)
+    bs = (ctypes.c_float * 4)(0.0, 0.0, 0.0, 0.0)
+    base = [3, ks, 1, P, P, P, 2, 1, 64, 128, 1000, qs, ws, bs, P, None, None]
+    for i in (1, 11, 12, 13):                       # the host arrays
+        a = list(base); a[i] = None
+        assert f(*a) == -1, i
+    for n in (0, 5):                                # n_idx outside 1..4
+        a = list(base); a[0] = n
+        assert f(*a) == -1
+    a = list(base); a[1] = arr(P, None, P, P)       # a NULL device pointer of one indexer
+    assert f(*a) == -1
+    assert b"indexer 1" in lib.lsa_last_error()
+    a = list(base); a[11] = arr(P, P, MISALIGNED, P)
+    assert f(*a) == -1
+    assert b"aligned" in lib.lsa_last_error()
+    a = list(base); a[14] = None                    # z_out
+    assert f(*a) == -1
+    a = list(base); a[6] = 70000                    # B too large
+    assert f(*a) == -2
+    # shapes outside the fused launch go through lsa_index_score's own checks
+    a = list(base); a[2] = 7                        # dtype
+    assert f(*a) == -1
+    assert b"lsa_index_score" in lib.lsa_last_error()

@@ -1,6 +1,7 @@
 """GPU parity of the widened rows against the CPU reference on identical inputs:
 the native re-score of the kept subset (lsa_index_rescore), the OR-mode union
-over several indexers (lsa_index_score with reduce_max = 2), and the
+over several indexers (lsa_index_score with reduce_max = 2, and
+lsa_index_score_union in one call), and the
 just-in-time fetch of the kept rows into a hot buffer (lsa_fetch_rows, with
 lsa_topk naming positions in the candidate list)."""
 import numpy as np
@@ -190,6 +191,67 @@ def test_union_over_indexers(ref, T, H, D, lens, dtype):
                                 wl.bias, reduce_max=True, want_prob=False, union_with=zr)
     torch.cuda.synchronize()
     check_scores(host(z), zr, host(p))
+
+
+def _union_calls(layers, fused):
+    """The union of `layers` on the GPU: one lsa_index_score_union call, or one
+    lsa_index_score call per indexer (the first writing, the rest combining)."""
+    wl0 = layers[0]
+    n = wl0.total_entries
+    z = torch.full((n,), float("nan"), device="cuda")
+    p = torch.full((n,), float("nan"), device="cuda")
+    krs, sl, es = dev(wl0.key_row_start), dev(wl0.seq_len), dev(wl0.entry_start)
+    keys = [dev(wl.keys) for wl in layers]
+    qs = [dev(wl.q) for wl in layers]
+    ws = [dev(wl.w) for wl in layers]
+    if fused:
+        lsa.lsa_index_score_union(keys, krs, sl, es, wl0.max_len, qs, ws,
+                                  [wl.bias for wl in layers], z, p)
+    else:
+        for i, wl in enumerate(layers):
+            lsa.lsa_index_score(keys[i], krs, sl, es, wl0.max_len, qs[i], ws[i], wl.bias,
+                                1 if i == 0 else 2, z, p if i == len(layers) - 1 else None)
+    torch.cuda.synchronize()
+    return host(z), host(p)
+
+
+@pytest.mark.parametrize("T,H,D,lens,n_layers,dtype", [
+    (1, 64, 128, [3000, 1, 777], 3, "bf16"),        # one launch: a few groups per wave
+    (1, 16, 64, [0, 2000, 33, 16, 17], 2, "bf16"),  # empty and ragged sequences, D = 64
+    (1, 40, 128, [5000, 4099], 4, "bf16"),          # padded head tile, four indexers
+    (1, 64, 128, [130000, 70000], 3, "bf16"),       # many groups per wave: ring crosses indexers
+    (1, 8, 128, [700], 1, "bf16"),                  # one indexer
+    (4, 64, 128, [513, 300], 3, "bf16"),            # several positions: one call per indexer
+    (1, 4, 32, [1024], 2, "f32"),                   # vector path
+])
+def test_union_single_call(ref, T, H, D, lens, n_layers, dtype):
+    """lsa_index_score_union equals, bit for bit, the per-indexer calls, and the
+    reference union of every indexer's gated score."""
+    layers = _layers(70 + T + H, len(lens), T, H, D, lens, n_layers, dtype)
+    announce(f"union single call T={T} H={H} D={D} lens={lens} n={n_layers} {dtype}")
+    zf, pf = _union_calls(layers, fused=True)
+    zs, ps = _union_calls(layers, fused=False)
+    np.testing.assert_array_equal(zf.view(np.uint32), zs.view(np.uint32))
+    np.testing.assert_array_equal(pf.view(np.uint32), ps.view(np.uint32))
+    wl0 = layers[0]
+    if wl0.total_entries <= 20000:
+        zr = None
+        for wl in layers:
+            zr, _ = ref.index_score(wl.keys, wl.key_row_start, wl.seq_len, wl.entry_start, wl.q,
+                                    wl.w, wl.bias, reduce_max=True, want_prob=False, union_with=zr)
+        check_scores(zf, zr, pf)
+        return
+    rng = np.random.default_rng(93)
+    for b in range(wl0.B):
+        S, es = int(wl0.seq_len[b]), int(wl0.entry_start[b])
+        s = np.sort(rng.choice(S, size=1200, replace=False))
+        zr = None
+        for wl in layers:
+            rows = wl.keys[int(wl.key_row_start[b]) + s]
+            zr, _ = ref.index_score(rows, np.zeros(1, np.int64), np.array([len(s)], np.int32),
+                                    np.zeros(1, np.int64), wl.q[b:b + 1], wl.w[b:b + 1], wl.bias,
+                                    reduce_max=True, want_prob=False, union_with=zr)
+        check_scores(zf[es + s], zr, pf[es + s])
 
 
 # ------------------------------------------------- just-in-time fetch of the kept rows
