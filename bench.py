@@ -220,7 +220,8 @@ def main():
     att_bytes = att_rows * wl.Dl * 2
     rl = max(1, -(-ROTATE_BYTES // att_bytes))
     if args.profile_launches:
-        rk, rl = 1, 1
+        # three key sets so the union's indexers read distinct keys, as in the timed runs
+        rk, rl = (3 if wl.T == 1 else 1), 1
     stream = torch.cuda.Stream()   # default priority
     with torch.cuda.stream(stream):
         d = DeviceInputs(wl, key_replicas=rk, latent_replicas=rl)

@@ -12,6 +12,9 @@
  *                          against every preceding compressed entry ("Scoring
  *                          Mechanism"), with the OR-union over positions of
  *                          section 2.4 "Optimal Configuration";
+ *   lsa_index_score_union -- the same score for the indexers of several
+ *                          layers at once, united by OR (section 2.4
+ *                          "Optimal Configuration");
  *   lsa_select_compact  -- keep every entry whose score reaches 0.5 ("Dynamic
  *                          Fetching"), as an ascending index list;
  *   lsa_index_rescore   -- the native indexer's per-step score of that
@@ -106,10 +109,10 @@ int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
                     int D, int64_t max_len, const void* q, const float* w, float bias,
                     int reduce_max, float* z_out, float* prob_out, void* stream);
 
-/* OR-union of several indexers' scores in one call (section 2.4
- * "Multi-Layer Indexers": a context entry is kept when the gate of any of the
- * indexers keeps it, and as sigmoid is monotone that is the gate on the
- * largest logit).  For l = 0 .. n_idx-1, indexer l has its own keys[l],
+/* OR-union of several indexers' scores in one call (section 2.4 "Optimal
+ * Configuration": the indexers of three intermediate layers, united by OR; an
+ * entry is kept when any indexer's gate keeps it, and as sigmoid is monotone
+ * that is the gate on the largest logit).  For l = 0 .. n_idx-1, indexer l has its own keys[l],
  * q[l], w[l] and bias[l], laid out as for lsa_index_score; all share the
  * sequence layout (key_row_start, seq_len, entry_start), dtype, B, T, H, D.
  *   z_out[entry_start[b] + s] = max over l and t of z_l[b,t,s];

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void k_score_decode(
 }
 
 // ------------------------------------------------------------ fused union
-// OR-mode union of up to kUnionMax indexers in one pass (T = 1): the decode
+// OR-mode union of up to kUnionMax indexers in one pass (T = 1; the indexers of
+// several layers united by OR, Technical Summary section 2.4): the decode
 // kernel's streaming with (indexer, group) as the unit.  A wave takes its
 // groups for indexer 0, then the same groups for indexer 1, ... ; the ring runs
 // on across the switch (the copies of the next indexer's first groups are in
@@ -658,6 +659,13 @@ extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dty
         if (!keys[l] || !q[l] || !w[l])
             return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: indexer %d has a NULL pointer",
                         l);
+    // what differs between the indexers is checked for all of them before anything
+    // is enqueued (the per-indexer calls below then fail on the first or not at all)
+    for (int l = 0; l < n_idx; ++l) {
+        if (!aligned16(keys[l]) || !aligned16(q[l]))
+            return fail(LSA_ERR_INVALID_ARG,
+                        "lsa_index_score_union: keys and q of indexer %d must be 16-byte aligned", l);
+    }
     const bool fused = dtype == LSA_DTYPE_BF16 && T == 1 && H <= 64 && (D == 64 || D == 128);
     if (!fused) {
         // other shapes: one score launch per indexer, each combining with the last
@@ -669,12 +677,6 @@ extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dty
             if (rc != LSA_OK) return rc;
         }
         return LSA_OK;
-    }
-    // the same validation as one score call, per indexer
-    for (int l = 0; l < n_idx; ++l) {
-        if (!aligned16(keys[l]) || !aligned16(q[l]))
-            return fail(LSA_ERR_INVALID_ARG,
-                        "lsa_index_score_union: keys and q of indexer %d must be 16-byte aligned", l);
     }
     if (!key_row_start || !seq_len || !entry_start || !z_out)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: a required pointer is NULL");
