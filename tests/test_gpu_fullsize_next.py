@@ -1,7 +1,7 @@
 """The widened rows at the full decode_500k size, in the launch configuration the
 benchmark times (the Pipeline object bench.py drives): the native re-score of
 the kept entries and its top-k, the just-in-time fetch from a pinned host pool,
-and attention over the fetched rows.
+attention over the fetched rows, and the OR-union of three indexers.
 
 The reference re-scores sampled kept entries one by one; the top-k is checked
 through properties that hold at any size; fetched rows are compared byte for
@@ -95,3 +95,35 @@ def test_fetch_and_attend_full_size(ref, run):
         outs.append((host(out), host(lse)))
     np.testing.assert_array_equal(outs[0][0], outs[1][0])
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
+def test_union_of_three_indexers_full_size(ref, run):
+    """Three indexers (the key pool and two row-rotated copies of it, so every
+    indexer scores different keys) united in one lsa_index_score_union launch:
+    bit-identical to the three combining launches, and the reference union on
+    sampled entries."""
+    wl, d, p = run
+    announce("full size decode_500k: union of three indexers, one launch and three")
+    keys = [d.keys[0]] + [torch.roll(d.keys[0], 7 * i + 1, dims=0) for i in (1, 2)]
+    args = (d.key_row_start, d.seq_len, d.entry_start, d.max_len)
+    z3 = torch.full_like(p.z, float("nan"))
+    for i, kk in enumerate(keys):
+        lsa.lsa_index_score(kk, *args, d.q, d.w, d.bias, 1 if i == 0 else 2, z3)
+    z1 = torch.full_like(p.z, float("nan"))
+    lsa.lsa_index_score_union(keys, *args, [d.q] * 3, [d.w] * 3, [d.bias] * 3, z1)
+    torch.cuda.synchronize()
+    z1, z3 = host(z1), host(z3)
+    np.testing.assert_array_equal(z1.view(np.uint32), z3.view(np.uint32))
+    keys_h = [host(kk) for kk in keys]
+    q, w = host(d.q), host(d.w)
+    rng = np.random.default_rng(13)
+    for b in range(wl.B):
+        S, es, krs = int(wl.seq_len[b]), int(wl.entry_start[b]), int(wl.key_row_start[b])
+        s = np.sort(rng.choice(S, size=300, replace=False))
+        zr = None
+        for kk in keys_h:
+            zr, _ = ref.index_score(kk[krs + s], np.zeros(1, np.int64),
+                                    np.array([len(s)], np.int32), np.zeros(1, np.int64),
+                                    q[b:b + 1], w[b:b + 1], d.bias, reduce_max=True,
+                                    want_prob=False, union_with=zr)
+        check_scores(z1[es + s].astype(np.float64), zr)
