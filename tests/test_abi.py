@@ -229,3 +229,17 @@ def test_score_union_validation(lib):
     a = list(base); a[2] = 7                        # dtype
     assert f(*a) == -1
     assert b"lsa_index_score" in lib.lsa_last_error()
+
+
+def test_union_binding_checks_its_lists():
+    """The Python wrapper refuses lists of different lengths before any pointer is taken."""
+    import torch
+    k = torch.zeros((4, 128), dtype=torch.bfloat16)
+    q = torch.zeros((1, 1, 2, 128), dtype=torch.bfloat16)
+    w = torch.zeros((1, 1, 2))
+    z = torch.zeros(4)
+    i64, i32 = torch.zeros(1, dtype=torch.int64), torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        binding.lsa_index_score_union([k, k], i64, i32, i64, 4, [q], [w, w], [0.0, 0.0], z)
+    with pytest.raises(ValueError):
+        binding.lsa_index_score_union([k], i64, i32, i64, 4, [q], [w], [0.0, 1.0], z)
