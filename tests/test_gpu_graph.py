@@ -1,4 +1,5 @@
-"""The four calls capture into a HIP graph and every replay matches the eager run."""
+"""The four calls, and the union of several indexers, capture into a HIP graph and every
+replay matches the eager run."""
 import numpy as np
 import pytest
 import torch
@@ -37,3 +38,35 @@ def test_graph_replays_match_eager():
                                  p.lse)]
         for a, b in zip(eager, got):
             np.testing.assert_array_equal(a, b, err_msg=f"replay {rep}")
+
+
+def test_graph_replays_of_the_union_match_eager():
+    """The single-launch union of three indexers (three key replicas) and the
+    per-indexer combining launches, each captured and replayed several times."""
+    wl = inputs.random_small(37, 2, 1, 64, 128, [9000, 4100], bias=-1.0)
+    d = DeviceInputs(wl, key_replicas=3)
+    # three different key sets: rotate the rows of the second and third replicas
+    for i in (1, 2):
+        d.keys[i].copy_(torch.roll(d.keys[0], 5 * i, dims=0))
+    p = Pipeline(d)
+    stream = torch.cuda.Stream()
+    for fused in (True, False):
+        announce(f"graph capture of the union of three indexers, fused={fused}")
+        with torch.cuda.stream(stream):
+            p.score_union(3, 0, fused=fused)
+        torch.cuda.synchronize()
+        eager = host(p.z).copy()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            p.score_union(3, 0, fused=fused)
+        for rep in range(3):
+            p.z.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(host(p.z).view(np.uint32), eager.view(np.uint32),
+                                          err_msg=f"replay {rep}")
+        if fused:
+            first = eager
+        else:
+            np.testing.assert_array_equal(first.view(np.uint32), eager.view(np.uint32))
