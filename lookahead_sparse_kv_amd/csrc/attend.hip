@@ -669,17 +669,24 @@ __global__ __launch_bounds__(CT) void k_attend_combine(int n_blocks, int nsplit,
 }
 
 // Vector path: one workgroup per (b, t, h); any Dl <= 1024, fp32 or bf16.
-template <typename E>
+// Wave w takes rows w, w+4, w+8, ... with its own online softmax (each lane
+// holds NPL = ceil(Dl/64) latent dims; the dot product is a wave reduction),
+// four rows in flight at a time; the four waves' (max, sum, output) merge
+// through LDS at the end.
+template <typename E, int NPL>
 __global__ __launch_bounds__(256) void k_attend_vector(
     const E* __restrict__ qa, int T, int Hq, int Dl, const E* __restrict__ latent,
     const int64_t* __restrict__ latent_row_start, const int32_t* __restrict__ topk_idx,
     const int32_t* __restrict__ topk_count, int k, const E* __restrict__ hca,
     const int64_t* __restrict__ hca_row_start, const int32_t* __restrict__ hca_count,
     int64_t max_hca, float scale, E* __restrict__ out, float* __restrict__ lse) {
-    __shared__ float red[4];
+    __shared__ float wml[2][4];
+    __shared__ float wo[4][64 * NPL];
     const int h = blockIdx.x % Hq;
     const int64_t bt = blockIdx.x / Hq;
     const int b = (int)(bt / T);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int ntop = min(topk_count[b], k);
     const int nh = hca ? (int)min((int64_t)hca_count[b], max_hca) : 0;
     const int n = ntop + nh;
@@ -687,44 +694,71 @@ __global__ __launch_bounds__(256) void k_attend_vector(
     const int64_t hrs = hca ? hca_row_start[b] : 0;
     const int32_t* idx = topk_idx + (int64_t)b * k;
     const E* qrow = qa + (bt * Hq + h) * Dl;
-    float qv[4], ov[4];
+    float qv[NPL], ov[NPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int d = threadIdx.x + 256 * i;
+    for (int i = 0; i < NPL; ++i) {
+        const int d = lane + 64 * i;
         qv[i] = d < Dl ? (float)qrow[d] : 0.0f;
         ov[i] = 0.0f;
     }
     float m = -INFINITY, l = 0.0f;
-    for (int j = 0; j < n; ++j) {
+    auto load_row = [&](int j, float (&rv)[NPL]) {
         const E* row = att_row<E>(j, ntop, n, latent, lrs, idx, hca, hrs, Dl);
-        float rv[4];
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) {
+            const int d = lane + 64 * i;
+            rv[i] = (row && d < Dl) ? (float)row[d] : 0.0f;
+        }
+    };
+    auto consume = [&](const float (&rv)[NPL]) {
         float part = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int d = threadIdx.x + 256 * i;
-            rv[i] = d < Dl ? (float)row[d] : 0.0f;
-            part += qv[i] * rv[i];
-        }
+        for (int i = 0; i < NPL; ++i) part += qv[i] * rv[i];
         for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-        __syncthreads();
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
-        __syncthreads();
-        const float logit = (red[0] + red[1] + red[2] + red[3]) * scale;
+        const float logit = part * scale;
         const float mn = fmaxf(m, logit);
         const float a = expf(m - mn);
         const float p = expf(logit - mn);
         l = l * a + p;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = ov[i] * a + p * rv[i];
+        for (int i = 0; i < NPL; ++i) ov[i] = ov[i] * a + p * rv[i];
         m = mn;
-    }
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    };
+    constexpr int RU = 4;                       // rows in flight per wave
+    for (int j = wave; j < n; j += 4 * RU) {
+        float rv[RU][NPL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int d = threadIdx.x + 256 * i;
-        if (d < Dl) out[(bt * Hq + h) * Dl + d] = (E)(ov[i] * inv);
+        for (int r = 0; r < RU; ++r) load_row(j + 4 * r, rv[r]);   // zeros past the end
+#pragma unroll
+        for (int r = 0; r < RU; ++r)
+            if (j + 4 * r < n) consume(rv[r]);
     }
-    if (threadIdx.x == 0 && lse) lse[bt * Hq + h] = l > 0.0f ? m + logf(l) : -INFINITY;
+    if (lane == 0) {
+        wml[0][wave] = m;
+        wml[1][wave] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) wo[wave][lane + 64 * i] = ov[i];
+    __syncthreads();
+    // merge: waves without rows (sum 0) get weight 0
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+        if (wml[1][w] > 0.0f) M = fmaxf(M, wml[0][w]);
+    float sc[4], L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        sc[w] = wml[1][w] > 0.0f ? expf(wml[0][w] - M) : 0.0f;
+        L += sc[w] * wml[1][w];
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    for (int d = threadIdx.x; d < Dl; d += 256) {
+        float o = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) o += sc[w] * wo[w][d];
+        out[(bt * Hq + h) * Dl + d] = (E)(o * inv);
+    }
+    if (threadIdx.x == 0 && lse) lse[bt * Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
 }
 
 // Split heuristic shared by the launch and the workspace query: groups of kMQ
@@ -857,15 +891,23 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
         return launch_status("attend_combine");
     }
     const unsigned blocks = (unsigned)((int64_t)B * T * Hq);
-    if (dtype == LSA_DTYPE_F32)
-        hipLaunchKernelGGL(k_attend_vector<float>, dim3(blocks), dim3(256), 0, st,
-                           (const float*)qa, T, Hq, Dl, (const float*)latent, latent_row_start,
-                           topk_idx, topk_count, k, (const float*)hca, hca_row_start, hca_count,
-                           hmax, scale, (float*)out, lse);
-    else
-        hipLaunchKernelGGL(k_attend_vector<bf16>, dim3(blocks), dim3(256), 0, st, (const bf16*)qa,
-                           T, Hq, Dl, (const bf16*)latent, latent_row_start, topk_idx, topk_count,
-                           k, (const bf16*)hca, hca_row_start, hca_count, hmax, scale, (bf16*)out,
-                           lse);
+#define LSA_ATTV(E, npl)                                                                       \
+    hipLaunchKernelGGL((k_attend_vector<E, npl>), dim3(blocks), dim3(256), 0, st,              \
+                       (const E*)qa, T, Hq, Dl, (const E*)latent, latent_row_start, topk_idx,  \
+                       topk_count, k, (const E*)hca, hca_row_start, hca_count, hmax, scale,    \
+                       (E*)out, lse)
+#define LSA_ATTV_NPL(E)                                                                        \
+    if (Dl <= 64) { LSA_ATTV(E, 1); }                                                          \
+    else if (Dl <= 128) { LSA_ATTV(E, 2); }                                                    \
+    else if (Dl <= 256) { LSA_ATTV(E, 4); }                                                    \
+    else if (Dl <= 512) { LSA_ATTV(E, 8); }                                                    \
+    else { LSA_ATTV(E, 16); }
+    if (dtype == LSA_DTYPE_F32) {
+        LSA_ATTV_NPL(float)
+    } else {
+        LSA_ATTV_NPL(bf16)
+    }
+#undef LSA_ATTV_NPL
+#undef LSA_ATTV
     return launch_status("attend_vector");
 }

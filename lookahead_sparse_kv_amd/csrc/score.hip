@@ -520,11 +520,20 @@ __global__ __launch_bounds__(256) void k_score_vector(
     float m = -INFINITY;
     for (int t = 0; t < T; ++t) {
         float u = 0.0f;
-        for (int h = 0; h < H; ++h) {
-            const float* qh = sq + (t * H + h) * D;
-            float dot = 0.0f;
-            for (int d = 0; d < D; ++d) dot += qh[d] * (float)row[d];
-            u += sw[t * H + h] * fmaxf(dot, 0.0f);
+        // eight heads per pass over the row: each key element is loaded once per
+        // pass, not once per head (head sums still added in head order)
+        for (int h0 = 0; h0 < H; h0 += 8) {
+            const int nh = min(8, H - h0);
+            const float* q0 = sq + (t * H + h0) * D;
+            float dot[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int d = 0; d < D; ++d) {
+                const float r = (float)row[d];
+#pragma unroll
+                for (int hh = 0; hh < 8; ++hh) dot[hh] += q0[min(hh, nh - 1) * D + d] * r;
+            }
+#pragma unroll
+            for (int hh = 0; hh < 8; ++hh)
+                if (hh < nh) u += sw[t * H + h0 + hh] * fmaxf(dot[hh], 0.0f);
         }
         const float z = u + bias;
         if (reduce_max) {
