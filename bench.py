@@ -203,7 +203,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by "
-              f"sequence with no exchange, see DESIGN.md", file=sys.stderr)
+              f"sequence with no exchange between GPUs, so one GPU's rate is the per-GPU rate",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     from lookahead_sparse_kv_amd import binding as lsa
