@@ -28,7 +28,7 @@ extern "C" {
 
 /* O1  Lookahead index score (TS 2.1 "Scoring Mechanism": a head-fused gated
  * matching score passed through a sigmoid; TS 5 "Architectural Constraints":
- * the query/key interaction is a dot product).  Instance fixed by this build:
+ * the query/key interaction is a dot product).  The instance computed here:
  *   u[b,t,s] = sum_h w[b,t,h] * max(0, sum_d q[b,t,h,d] * k[b,s,d])
  *   z = u + bias,   I = 1 / (1 + exp(-z)).
  * keys: pool of rows of D elements; sequence b's entry s is row
@@ -52,7 +52,7 @@ int lsa_ref_index_score(const void* keys, int dtype, const int64_t* key_row_star
 /* O1b Native re-score of the kept subset (TS 2.1 "Tiered Selection": inside
  * the fetched subset the backbone's native Lightning Indexer takes a
  * fine-grained top-k; TS 2.3: the compressed indexer keys are the frozen
- * keys K_IComp, shared with the Memory Indexer).  This build's reading: the
+ * keys K_IComp, shared with the Memory Indexer).  The reading taken here: the
  * native indexer scores a candidate with its own per-step queries q' and
  * weights w' against the same key rows, as a plain ranking logit (no bias,
  * no sigmoid):
