@@ -5,13 +5,31 @@
  * the page "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long Context via
  * Lookahead Sparse Attention" (gist.science), Technical Summary 2.1 and 2.4.
  *
- * Built with plain gcc, no -ffast-math, no intrinsics, no threads.
+ * Built with plain gcc, no -ffast-math, no intrinsics.  The same source is
+ * built twice: once single-threaded (the parity build; the OpenMP pragmas
+ * below are then ignored) and once with -fopenmp (the timing build, and the
+ * build the full-size tests use).  The pragmas only share out iterations of
+ * loops whose iterations are independent -- queries, entries, sequences,
+ * (position, head) rows -- so every output element is computed by the same
+ * scalar operations in the same order in both builds.
  */
 #include "lsa_oracle.h"
 
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops below may use (1 in the single-threaded build). */
+int lsa_ref_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* Exact widening of one stored element to double. */
 static double load_elem(const void* base, int dtype, int64_t i) {
@@ -34,6 +52,7 @@ int lsa_ref_query_encode(const void* h, int dtype, int M, int d_model, int r, in
                          double* c_out, double* q_out, double* w_out) {
     if (!h || !w_down || !w_up || !w_gate || !c_out || !q_out || !w_out) return -1;
     if (M <= 0 || d_model <= 0 || r <= 0 || H <= 0 || D <= 0 || !dtype_ok(dtype)) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int m = 0; m < M; ++m) {
         const int64_t hrow = (int64_t)m * d_model;
         /* the low-rank latent of this token */
@@ -78,6 +97,7 @@ int lsa_ref_index_score(const void* keys, int dtype, const int64_t* key_row_star
 
     for (int b = 0; b < B; ++b) {
         const int64_t S = seq_len[b];
+#pragma omp parallel for schedule(dynamic, 256)
         for (int64_t s = 0; s < S; ++s) {
             const int64_t krow = (key_row_start[b] + s) * (int64_t)D;
             double m = -INFINITY;
@@ -124,6 +144,7 @@ int lsa_ref_index_rescore(const void* keys, int dtype, const int64_t* key_row_st
         return -1;
     if (B <= 0 || H <= 0 || D <= 0 || !dtype_ok(dtype)) return -1;
     for (int b = 0; b < B; ++b) {
+#pragma omp parallel for schedule(dynamic, 64)
         for (int32_t j = 0; j < cand_count[b]; ++j) {
             const int32_t s = cand_idx[entry_start[b] + j];
             const int64_t krow = (key_row_start[b] + s) * (int64_t)D;
@@ -188,11 +209,18 @@ int lsa_ref_topk(const double* r, const int64_t* entry_start, const int32_t* seq
     if (!r || !entry_start || !seq_len || !cand_idx || !cand_count || !topk_idx || !topk_count)
         return -1;
     if (B <= 0 || k <= 0) return -1;
+    for (int b = 0; b < B; ++b)
+        if (cand_count[b] < 0 || cand_count[b] > seq_len[b]) return -1;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1)
     for (int b = 0; b < B; ++b) {
         const int32_t n = cand_count[b];
-        if (n < 0 || n > seq_len[b]) return -1;
         ranked_t* items = (ranked_t*)malloc(sizeof(ranked_t) * (size_t)(n > 0 ? n : 1));
-        if (!items) return -1;
+        if (!items) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
         for (int32_t j = 0; j < n; ++j) {
             const int32_t s = cand_idx[entry_start[b] + j];
             items[j].s = s;
@@ -207,7 +235,7 @@ int lsa_ref_topk(const double* r, const int64_t* entry_start, const int32_t* seq
         topk_count[b] = keep;
         free(items);
     }
-    return 0;
+    return failed ? -1 : 0;
 }
 
 /* O4 -- TS 2.1 final core attention over the top-k entries plus all HCA rows. */
@@ -221,6 +249,7 @@ int lsa_ref_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int D
     if (B <= 0 || T <= 0 || Hq <= 0 || Dl <= 0 || k <= 0 || !dtype_ok(dtype)) return -1;
     if (hca && (!hca_row_start || !hca_count)) return -1;
 
+    int failed = 0;
     for (int b = 0; b < B; ++b) {
         const int32_t nt = topk_count[b];
         const int32_t nh = hca ? hca_count[b] : 0;
@@ -228,8 +257,11 @@ int lsa_ref_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int D
         /* element offset of attended row j */
         int64_t* row_off = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
         const void** row_src = (const void**)malloc(sizeof(void*) * (size_t)(n > 0 ? n : 1));
-        double* logit = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
-        if (!row_off || !row_src || !logit) return -1;
+        if (!row_off || !row_src) {
+            free(row_off);
+            free((void*)row_src);
+            return -1;
+        }
         for (int32_t j = 0; j < nt; ++j) {
             row_src[j] = latent;
             row_off[j] = (latent_row_start[b] + topk_idx[(int64_t)b * k + j]) * (int64_t)Dl;
@@ -238,8 +270,18 @@ int lsa_ref_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int D
             row_src[nt + i] = hca;
             row_off[nt + i] = (hca_row_start[b] + i) * (int64_t)Dl;
         }
-        for (int t = 0; t < T; ++t) {
-            for (int h = 0; h < Hq; ++h) {
+        /* every (position, head) row of sequence b is independent of the others */
+#pragma omp parallel
+        {
+            double* logit = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+            if (!logit) {
+#pragma omp atomic write
+                failed = 1;
+            }
+#pragma omp for schedule(dynamic, 1)
+            for (int th = 0; th < T * Hq; ++th) {
+                if (!logit) continue;
+                const int t = th / Hq, h = th % Hq;
                 const int64_t qoff = (((int64_t)b * T + t) * Hq + h) * (int64_t)Dl;
                 double* o = out + qoff;
                 for (int d = 0; d < Dl; ++d) o[d] = 0.0;
@@ -265,12 +307,12 @@ int lsa_ref_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int D
                 for (int d = 0; d < Dl; ++d) o[d] /= Z;
                 if (lse) lse[lidx] = mu + log(Z);
             }
+            free(logit);
         }
         free(row_off);
-        free(row_src);
-        free(logit);
+        free((void*)row_src);
     }
-    return 0;
+    return failed ? -1 : 0;
 }
 
 /* O5 -- TS 2.1 "Dynamic Fetching": the kept rows, copied in list order. */

@@ -26,6 +26,10 @@
 extern "C" {
 #endif
 
+/* Threads the oracle's loops may use: 1 in the single-threaded parity build,
+ * the OpenMP thread count in the timing build (same source, -fopenmp). */
+int lsa_ref_max_threads(void);
+
 /* O1  Lookahead index score (TS 2.1 "Scoring Mechanism": a head-fused gated
  * matching score passed through a sigmoid; TS 5 "Architectural Constraints":
  * the query/key interaction is a dot product).  The instance computed here:

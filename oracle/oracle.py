@@ -23,17 +23,26 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 
 
+_LIB_MT_PATH = os.path.join(_HERE, "liblsa_oracle_omp.so")
+_CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-Wall", "-Wextra"]
+
+
+def _stale(lib: str) -> bool:
+    return not os.path.exists(lib) or os.path.getmtime(lib) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "lsa_oracle.h")))
+
+
 def build(force: bool = False) -> str:
-    """Compile the oracle with plain gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
-        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "lsa_oracle.h"))
-    ):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(
-            ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-             "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-        )
-        os.replace(tmp, _LIB_PATH)
+    """Compile the oracle with plain gcc (no fast-math, no FMA contraction), twice:
+    single-threaded (the OpenMP pragmas ignored) and with -fopenmp.  Both builds
+    run the same scalar operations per output element; the second only shares
+    out independent iterations among threads."""
+    for lib, extra in ((_LIB_PATH, ["-Wno-unknown-pragmas"]), (_LIB_MT_PATH, ["-fopenmp"])):
+        if force or _stale(lib):
+            tmp = lib + ".tmp"
+            subprocess.check_call(["gcc"] + _CFLAGS + extra + ["-o", tmp, _SRC, "-lm"])
+            os.replace(tmp, lib)
     return _LIB_PATH
 
 
@@ -49,6 +58,8 @@ def _bind(path):
     lib.lsa_ref_query_encode.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, P]
     lib.lsa_ref_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, D, P, P]
     lib.lsa_ref_index_rescore.argtypes = [P, I, P, P, P, P, I, I, I, P, P, P]
+    lib.lsa_ref_max_threads.argtypes = []
+    lib.lsa_ref_max_threads.restype = ctypes.c_int
     for f in (lib.lsa_ref_index_score, lib.lsa_ref_select, lib.lsa_ref_topk,
               lib.lsa_ref_sparse_attend, lib.lsa_ref_index_rescore, lib.lsa_ref_fetch_rows,
               lib.lsa_ref_query_encode):
@@ -57,18 +68,47 @@ def _bind(path):
 
 
 _default_lib = None
+_mt_lib = None
 _lib_override = None
+_threaded = False
 
 
 def _load():
-    """The compiled reference; tests may point it at another build with use_library()."""
-    global _default_lib
+    """The compiled reference: the single-threaded build, or the OpenMP build inside
+    `with threads():`; tests may point it at another build with use_library()."""
+    global _default_lib, _mt_lib
     if _lib_override is not None:
         return _lib_override
+    if _threaded:
+        if _mt_lib is None:
+            build()
+            _mt_lib = _bind(_LIB_MT_PATH)
+        return _mt_lib
     if _default_lib is None:
         build()
         _default_lib = _bind(_LIB_PATH)
     return _default_lib
+
+
+class threads:
+    """Context manager: calls inside it run on the OpenMP build (all cores, or
+    OMP_NUM_THREADS).  Results are bit-identical to the single-threaded build."""
+
+    def __enter__(self):
+        global _threaded
+        self._prev = _threaded
+        _threaded = True
+        return self
+
+    def __exit__(self, *exc):
+        global _threaded
+        _threaded = self._prev
+        return False
+
+
+def max_threads() -> int:
+    """Threads the currently selected build may use (1 for the single-threaded one)."""
+    return int(_load().lsa_ref_max_threads())
 
 
 def use_library(path):
