@@ -33,12 +33,24 @@ def _stale(lib: str) -> bool:
         os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "lsa_oracle.h")))
 
 
+# LSA_ORACLE_SANITIZE=1 swaps the single-threaded build for one instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must preload the
+# ASan runtime); the sanitizer test runs the pins against it in a subprocess.
+_SANITIZE = os.environ.get("LSA_ORACLE_SANITIZE") == "1"
+if _SANITIZE:
+    _LIB_PATH = os.path.join(_HERE, "liblsa_oracle_asan.so")
+
+
 def build(force: bool = False) -> str:
     """Compile the oracle with plain gcc (no fast-math, no FMA contraction), twice:
     single-threaded (the OpenMP pragmas ignored) and with -fopenmp.  Both builds
     run the same scalar operations per output element; the second only shares
     out independent iterations among threads."""
-    for lib, extra in ((_LIB_PATH, ["-Wno-unknown-pragmas"]), (_LIB_MT_PATH, ["-fopenmp"])):
+    single = ["-Wno-unknown-pragmas"]
+    if _SANITIZE:
+        single += ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                   "-fno-omit-frame-pointer", "-g"]
+    for lib, extra in ((_LIB_PATH, single), (_LIB_MT_PATH, ["-fopenmp"])):
         if force or _stale(lib):
             tmp = lib + ".tmp"
             subprocess.check_call(["gcc"] + _CFLAGS + extra + ["-o", tmp, _SRC, "-lm"])
