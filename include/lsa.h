@@ -54,8 +54,9 @@
  *   output is touched, and lsa_last_error() describes the problem.  Faults
  *   inside kernels surface at the caller's next synchronisation.
  * - Calls are reentrant and hold no global mutable state besides a
- *   thread-local error message and a per-device cache of the device's
- *   properties.
+ *   thread-local error message, a per-device cache of the device's
+ *   properties, and the built-in scratch array of lsa_select_compact_noalloc
+ *   (one per GPU).
  */
 #ifndef LSA_H
 #define LSA_H
@@ -192,6 +193,19 @@ int lsa_select_compact(const float* z, const int64_t* entry_start, const int32_t
                        int B, int64_t max_len, float threshold, int32_t* cand_idx,
                        int32_t* cand_count, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/* lsa_select_compact without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as
+ * lsa_select_compact, minus the workspace: the per-tile counts live in a
+ * built-in device array of 2^18 int32 (1 MiB per GPU, held until the process
+ * ends), so B * ceil(max_len / 2048) must not exceed 262144 (else
+ * UNSUPPORTED).  The call allocates nothing.  Calls that overlap on one GPU
+ * (other streams, other host threads) share that array and race; serialise
+ * them.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int lsa_select_compact_noalloc(const float* z, const int64_t* entry_start,
+                               const int32_t* seq_len, int B, int64_t max_len, float threshold,
+                               int32_t* cand_idx, int32_t* cand_count, void* stream);
 
 /* Tiered selection (section 2.1): the top-k candidates of each sequence by
  * rank key r[entry_start[b] + s] (fp32; the pipeline passes the indexer logit

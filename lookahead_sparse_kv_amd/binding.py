@@ -28,7 +28,7 @@ LSA_OP_TOPK = 2
 LSA_OP_ATTEND = 3
 
 EXPORTED = ["lsa_query_encode", "lsa_index_score", "lsa_index_score_union", "lsa_index_rescore",
-            "lsa_select_compact", "lsa_topk", "lsa_fetch_rows",
+            "lsa_select_compact", "lsa_select_compact_noalloc", "lsa_topk", "lsa_fetch_rows",
             "lsa_sparse_attend",
             "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
 
@@ -57,6 +57,7 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_index_score_union.argtypes = [I, P, I, P, P, P, I, I, I, I, L, P, P, P, P, P, P]
     lib.lsa_index_rescore.argtypes = [P, I, P, P, P, P, P, I, I, I, L, P, P, P, P]
     lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
+    lib.lsa_select_compact_noalloc.argtypes = [P, P, P, I, L, F, P, P, P]
     lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, I, P, Z, P]
     lib.lsa_fetch_rows.argtypes = [P, L, P, P, P, P, I, L, P, P, P]
     lib.lsa_query_encode.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P]
@@ -69,7 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_last_error.restype = ctypes.c_char_p
     lib.lsa_version.argtypes = []
     lib.lsa_version.restype = I
-    for name in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact", "lsa_topk",
+    for name in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact",
+                 "lsa_select_compact_noalloc", "lsa_topk",
                  "lsa_fetch_rows", "lsa_query_encode",
                  "lsa_sparse_attend"):
         getattr(lib, name).restype = I
@@ -215,6 +217,21 @@ def lsa_select_compact(z, entry_start, seq_len, max_len: int, cand_idx, cand_cou
                                 float(threshold), _ptr(cand_idx), _ptr(cand_count),
                                 _ptr(workspace), ws_bytes, _stream(stream))
     _check("lsa_select_compact", rc)
+    return cand_idx, cand_count
+
+
+def lsa_select_compact_noalloc(z, entry_start, seq_len, max_len: int, cand_idx, cand_count,
+                               threshold: float = 0.0, stream=None):
+    """lsa_select_compact with the library's built-in scratch instead of a workspace."""
+    lib = load_library()
+    _dev(z, "z", torch.float32)
+    _dev(cand_idx, "cand_idx", torch.int32)
+    _dev(cand_count, "cand_count", torch.int32)
+    B = seq_len.numel()
+    rc = lib.lsa_select_compact_noalloc(_ptr(z), _ptr(entry_start), _ptr(seq_len), B,
+                                        int(max_len), float(threshold), _ptr(cand_idx),
+                                        _ptr(cand_count), _stream(stream))
+    _check("lsa_select_compact_noalloc", rc)
     return cand_idx, cand_count
 
 

@@ -11,6 +11,8 @@
 //            values, from L2), then writes its kept indices in ascending
 //            order through a workgroup-wide exclusive scan.
 // The order of the output never depends on scheduling.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace lsa {
@@ -154,34 +156,108 @@ size_t lsa_select_workspace(int B, int64_t max_len) {
     return sizeof(int32_t) * (size_t)B * (size_t)select_tiles(max_len);
 }
 
+// The two launches (count, then scatter), with the per-tile counts in `tc`.
+static int select_launch(const char* who, const float* z, const int64_t* entry_start,
+                         const int32_t* seq_len, int B, int64_t max_len, float threshold,
+                         int32_t* cand_idx, int32_t* cand_count, int32_t* tc, hipStream_t st) {
+    const int ntiles = (int)select_tiles(max_len);
+    dim3 grid((unsigned)ntiles, (unsigned)B);
+    hipLaunchKernelGGL(k_select_count, grid, dim3(kSelThreads), 0, st, z, entry_start, seq_len,
+                       max_len, threshold, ntiles, tc);
+    int rc = launch_status(who);
+    if (rc != LSA_OK) return rc;
+    hipLaunchKernelGGL(k_select_scatter, grid, dim3(kSelThreads), 0, st, z, entry_start, seq_len,
+                       max_len, threshold, ntiles, tc, cand_idx, cand_count);
+    return launch_status(who);
+}
+
+static int select_validate(const char* who, const float* z, const int64_t* entry_start,
+                           const int32_t* seq_len, int B, int64_t max_len,
+                           const int32_t* cand_idx, const int32_t* cand_count) {
+    if (!z || !entry_start || !seq_len || !cand_idx || !cand_count)
+        return fail(LSA_ERR_INVALID_ARG, "%s: a required pointer is NULL", who);
+    if (B <= 0 || max_len < 0)
+        return fail(LSA_ERR_INVALID_ARG, "%s: B=%d max_len=%lld", who, B, (long long)max_len);
+    if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "%s: B=%d > 65535", who, B);
+    if (max_len > (int64_t)1 << 31) return fail(LSA_ERR_UNSUPPORTED, "%s: max_len too large", who);
+    return LSA_OK;
+}
+
 extern "C" int lsa_select_compact(const float* z, const int64_t* entry_start,
                                   const int32_t* seq_len, int B, int64_t max_len, float threshold,
                                   int32_t* cand_idx, int32_t* cand_count, void* workspace,
                                   size_t workspace_bytes, void* stream) {
     clear_error();
-    if (!z || !entry_start || !seq_len || !cand_idx || !cand_count)
-        return fail(LSA_ERR_INVALID_ARG, "lsa_select_compact: a required pointer is NULL");
-    if (B <= 0 || max_len < 0)
-        return fail(LSA_ERR_INVALID_ARG, "lsa_select_compact: B=%d max_len=%lld", B,
-                    (long long)max_len);
-    if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "lsa_select_compact: B=%d > 65535", B);
-    if (max_len > (int64_t)1 << 31)
-        return fail(LSA_ERR_UNSUPPORTED, "lsa_select_compact: max_len too large");
+    int rc = select_validate("lsa_select_compact", z, entry_start, seq_len, B, max_len, cand_idx,
+                             cand_count);
+    if (rc != LSA_OK) return rc;
     const size_t need = lsa_select_workspace(B, max_len);
     if (!workspace || workspace_bytes < need)
         return fail(LSA_ERR_WORKSPACE, "lsa_select_compact: workspace %zu < %zu bytes",
                     workspace_bytes, need);
-    int rc = check_device(nullptr);
+    rc = check_device(nullptr);
     if (rc != LSA_OK) return rc;
-    hipStream_t st = (hipStream_t)stream;
-    const int ntiles = (int)select_tiles(max_len);
-    dim3 grid((unsigned)ntiles, (unsigned)B);
-    int32_t* tc = (int32_t*)workspace;
-    hipLaunchKernelGGL(k_select_count, grid, dim3(kSelThreads), 0, st, z, entry_start, seq_len,
-                       max_len, threshold, ntiles, tc);
-    rc = launch_status("select_count");
+    return select_launch("lsa_select_compact", z, entry_start, seq_len, B, max_len, threshold,
+                         cand_idx, cand_count, (int32_t*)workspace, (hipStream_t)stream);
+}
+
+// ------------------------------------------------- no-allocation variant
+// The per-tile counts of lsa_select_compact_noalloc live in this file-scope
+// device array (one copy per GPU, held until the process ends).  Its name is
+// a host-side stand-in in host code: kernels get its device address, taken
+// once per device with hipGetSymbolAddress.  Every tile count a call reads
+// is written earlier in the same call, so nothing needs clearing between
+// calls; calls that overlap on one GPU share the array and race.
+namespace lsa {
+constexpr int64_t kSelScratchTiles = (int64_t)1 << 18;   // 1 MiB of int32 tile counts
+static __device__ __align__(256) int32_t scratch[kSelScratchTiles];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+// The device address of `scratch` on the current device (set up on first use).
+static int scratch_address(const char* who, int32_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LSA_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(LSA_ERR_UNSUPPORTED, "%s: device id %d", who, dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(LSA_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = (int32_t*)ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LSA_OK;
+}
+}  // namespace lsa
+
+extern "C" int lsa_select_compact_noalloc(const float* z, const int64_t* entry_start,
+                                          const int32_t* seq_len, int B, int64_t max_len,
+                                          float threshold, int32_t* cand_idx,
+                                          int32_t* cand_count, void* stream) {
+    clear_error();
+    const char* who = "lsa_select_compact_noalloc";
+    int rc = select_validate(who, z, entry_start, seq_len, B, max_len, cand_idx, cand_count);
     if (rc != LSA_OK) return rc;
-    hipLaunchKernelGGL(k_select_scatter, grid, dim3(kSelThreads), 0, st, z, entry_start, seq_len,
-                       max_len, threshold, ntiles, tc, cand_idx, cand_count);
-    return launch_status("select_scatter");
+    const int64_t tiles = (int64_t)B * select_tiles(max_len);
+    if (tiles > kSelScratchTiles)
+        return fail(LSA_ERR_UNSUPPORTED,
+                    "%s: B * ceil(max_len / %d) = %lld tiles exceed the built-in scratch of %lld "
+                    "(use lsa_select_compact with a workspace)",
+                    who, kTile, (long long)tiles, (long long)kSelScratchTiles);
+    rc = check_device(nullptr);
+    if (rc != LSA_OK) return rc;
+    int32_t* tc = nullptr;
+    rc = scratch_address(who, &tc);
+    if (rc != LSA_OK) return rc;
+    return select_launch(who, z, entry_start, seq_len, B, max_len, threshold, cand_idx,
+                         cand_count, tc, (hipStream_t)stream);
 }

@@ -87,6 +87,19 @@ def test_select_validation(lib):
     assert f(P, P, P, 4, 100000, 0.0, P, P, None, need, None) == -3
 
 
+def test_select_noalloc_validation(lib):
+    P = FAKE
+    f = lib.lsa_select_compact_noalloc
+    assert f(None, P, P, 1, 10, 0.0, P, P, None) == -1
+    assert f(P, P, P, 0, 10, 0.0, P, P, None) == -1
+    assert f(P, P, P, 1, -1, 0.0, P, P, None) == -1
+    # the built-in scratch holds 2^18 tile counts (2048 entries each): 5 sequences of
+    # 2^27 entries need 5 x 2^16 of them
+    assert f(P, P, P, 70000, 10, 0.0, P, P, None) == -2                      # B too large
+    assert f(P, P, P, 5, 1 << 27, 0.0, P, P, None) == -2
+    assert b"scratch" in lib.lsa_last_error()
+
+
 def test_topk_validation(lib):
     P = FAKE
     f = lib.lsa_topk
