@@ -123,7 +123,8 @@ int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
  * (H <= 64, D in {64, 128}) stream every indexer's keys in one launch and
  * keep the running maximum in registers, so z_out is written once; the
  * result is bit-identical to calling lsa_index_score once per indexer
- * (reduce_max = 1, then 2).  Other shapes make exactly those calls.
+ * (reduce_max = 1, then 2), NaN logits included (an entry that every indexer
+ * scores NaN stays NaN).  Other shapes make exactly those calls.
  * Envelope: 1 <= n_idx <= 4; otherwise as lsa_index_score.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 int lsa_index_score_union(int n_idx, const void* const* keys, int dtype,
@@ -263,8 +264,9 @@ int lsa_fetch_rows(const void* src, int64_t row_bytes, const int64_t* src_row_st
  *   out [B, T, Hq, Dl] in `dtype`; lse [B, T, Hq] fp32 or NULL.
  *   workspace  lsa_workspace_bytes(LSA_OP_ATTEND, B, T, Hq, Dl, 0, k, max_hca)
  *              bytes (split partial results); may be 0 for some shapes.
- * Envelope: the bf16 matrix-core path takes Hq <= 64 and Dl in {128, 256,
- * 512}; other shapes (and fp32) use the vector path (Dl <= 1024).
+ * Envelope: the bf16 matrix-core path takes Dl in {128, 256, 512} and any Hq
+ * (a sequence's T*Hq query rows are taken 64 at a time); other shapes (and
+ * fp32) use the vector path (Dl <= 1024).
  * Errors: INVALID_ARG, UNSUPPORTED, WORKSPACE, HIP. */
 int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int Dl,
                       const void* latent, const int64_t* latent_row_start,

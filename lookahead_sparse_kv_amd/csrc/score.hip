@@ -309,10 +309,13 @@ __global__ __launch_bounds__(256) void k_score_union(
             sacc += __shfl_xor(sacc, 16);
             sacc += __shfl_xor(sacc, 32);
             const float z = sacc + bias;
-            // every lane holds entry n16's logit; lane 16 (i % 4) + n16 keeps it
+            // every lane holds entry n16's logit; lane 16 (i % 4) + n16 keeps it.
+            // Indexer 0's logit is taken as it is and later ones are folded in with
+            // fmaxf, exactly as the per-indexer calls combine them (so a NaN from
+            // every indexer stays NaN, and a NaN from some yields the others' max).
 #pragma unroll
             for (int s8 = 0; s8 < ZS; ++s8)
-                if ((i >> 2) == s8 && (i & 3) == g) zmax[s8] = fmaxf(zmax[s8], z);
+                if ((i >> 2) == s8 && (i & 3) == g) zmax[s8] = l == 0 ? z : fmaxf(zmax[s8], z);
         }
     }
 #pragma unroll

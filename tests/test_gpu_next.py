@@ -254,6 +254,28 @@ def test_union_single_call(ref, T, H, D, lens, n_layers, dtype):
         check_scores(zf[es + s], zr, pf[es + s])
 
 
+def test_union_nan_logits_match_per_indexer_calls():
+    """NaN logits: the fused launch combines them as the per-indexer calls do.  A NaN
+    gate weight makes every logit of that (sequence, indexer) NaN: sequence 0 is NaN
+    for indexer 0 only, sequence 1 for every indexer, sequence 2 for the last."""
+    layers = _layers(171, 3, 1, 64, 128, [3000, 1000, 777], 3)
+    layers[0].w[0, 0, 5] = np.nan
+    for wl in layers:
+        wl.w[1, 0, 0] = np.nan
+    layers[-1].w[2, 0, 63] = np.nan
+    announce("union with NaN logits")
+    zf, pf = _union_calls(layers, fused=True)
+    zs, ps = _union_calls(layers, fused=False)
+    for a, b in ((zf, zs), (pf, ps)):
+        nan = np.isnan(a)
+        np.testing.assert_array_equal(nan, np.isnan(b))
+        np.testing.assert_array_equal(a[~nan].view(np.uint32), b[~nan].view(np.uint32))
+    es = layers[0].entry_start
+    assert not np.isnan(zf[es[0]:es[0] + 3000]).any()      # the other indexers' max
+    assert np.isnan(zf[es[1]:es[1] + 1000]).all()          # NaN from every indexer
+    assert not np.isnan(zf[es[2]:es[2] + 777]).any()
+
+
 # ------------------------------------------------- just-in-time fetch of the kept rows
 
 def _ws(op, B, *args, **kw):

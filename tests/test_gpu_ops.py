@@ -278,7 +278,7 @@ def test_attend_tiny_fp32(ref):
     (1, 1, 64, 512, [100], [0], [0], 16),                        # nothing to attend
     (4, 1, 8, 96, [80, 80, 80, 80], [10, 0, 80, 1], [3, 0, 0, 2], 80),  # vector path, bf16
     (2, 4, 64, 512, [3000, 2500], [700, 2048], [200, 50], 2048),  # 4 positions, row splits
-    (1, 1, 96, 512, [600], [300], [40], 512),                    # 3 groups of 32 query rows
+    (1, 1, 96, 512, [600], [300], [40], 512),                    # 2 groups of query rows: 64, then 32
     (3, 5, 7, 128, [90, 200, 64], [90, 3, 64], [1, 0, 9], 96),   # 35 query rows per sequence
 ])
 def test_attend_bf16(ref, B, T, Hq, Dl, lens, counts, hca, k):
