@@ -3,16 +3,23 @@
 One step = one pass of the whole path over one batch: index score (max over
 positions) -> gate + compaction -> top-k -> sparse attention, all enqueued on
 one stream.  Also timed, outside the step: the native indexer's per-step
-re-score of the kept entries with its top-k, and the OR-mode union of three
-indexers (three score launches).  The default workload is 8 sequences at 500K tokens (125000
-compressed entries each, 3907 HCA rows, top-k 2048, latent 512, 64 heads).
+re-score of the kept entries with its top-k, the OR-mode union of three
+indexers, the query encoder, the cold-pool fetch, and -- on its own workload
+(16 sequences x 64 positions against one shared set of 65536 entries) -- the
+tau-burst trigger score on the matrix cores.  The default workload is 8
+sequences at 500K tokens (125000 compressed entries each, 3907 HCA rows, top-k
+2048, latent 512, 64 heads).
 
 Prints one JSON line.  `value` = indexer scores per second of whole steps
 (sum of S_b per step / step time).  The roofline object covers the score
-kernel, the dominant one by bytes; the attention kernel gets a second one.
-Inputs are resident in HBM before timing; key and latent pools are replicated
-and rotated so each timed launch reads memory the 256 MB on-die cache does
-not hold.  Timed work is replayed from HIP graphs captured on one stream.
+kernel, the dominant one by bytes; attention, re-score, union, encoder and
+the tau-burst score get their own.  HBM fractions are given against the
+8 TB/s peak and against a 1 GiB read and a 1 GiB copy measured in the same
+run.  Inputs are resident in HBM before timing; key and latent pools are
+replicated and rotated so each timed launch reads memory the 256 MB on-die
+cache does not hold.  Timed work is replayed from HIP graphs captured on one
+stream; `latency_us` times single calls from one-launch graphs.  The CPU
+baseline is the reference on all host cores, with its one-thread figure.
 """
 from __future__ import annotations
 
@@ -174,29 +181,159 @@ def timed_graph(torch, stream, g, launches, intervals=7, warm=2):
 
 
 def cpu_baseline(wl, nseq: int):
-    """The CPU reference as it stands (single thread) on sequences 0..nseq-1 of the workload:
-    score, gate, top-k and attention of those sequences; returned as scores/s."""
+    """The CPU reference as it stands on sequences 0..nseq-1 of the workload: score,
+    gate, top-k and attention of those sequences, on all host cores (its OpenMP
+    build) and on one thread (its single-threaded build; the same arithmetic);
+    returned as scores/s."""
     from oracle import oracle
     oracle.build()
     nseq = min(nseq, wl.B)
-    t0 = time.perf_counter()
-    for b in range(nseq):
-        S = int(wl.seq_len[b])
-        kr = int(wl.key_row_start[b])
-        z, _ = oracle.index_score(wl.keys[kr:kr + S], np.zeros(1, np.int64), wl.seq_len[b:b + 1],
-                                  np.zeros(1, np.int64), wl.q[b:b + 1], wl.w[b:b + 1], wl.bias,
+    hca = wl.hca is not None
+
+    def path():
+        z, _ = oracle.index_score(wl.keys, wl.key_row_start[:nseq], wl.seq_len[:nseq],
+                                  wl.entry_start[:nseq], wl.q[:nseq], wl.w[:nseq], wl.bias,
                                   reduce_max=True, want_prob=False)
-        c, n = oracle.select(z, np.zeros(1, np.int64), wl.seq_len[b:b + 1])
-        t, tn = oracle.topk(z, np.zeros(1, np.int64), wl.seq_len[b:b + 1], c, n, wl.k)
-        oracle.sparse_attend(wl.qa[b:b + 1], wl.latent, wl.latent_row_start[b:b + 1], t, tn, wl.k,
-                             wl.hca, None if wl.hca is None else wl.hca_row_start[b:b + 1],
-                             None if wl.hca is None else wl.hca_count[b:b + 1], wl.scale)
-    dt = time.perf_counter() - t0
+        c, n = oracle.select(z, wl.entry_start[:nseq], wl.seq_len[:nseq])
+        t, tn = oracle.topk(z, wl.entry_start[:nseq], wl.seq_len[:nseq], c, n, wl.k)
+        oracle.sparse_attend(wl.qa[:nseq], wl.latent, wl.latent_row_start[:nseq], t, tn, wl.k,
+                             wl.hca, wl.hca_row_start[:nseq] if hca else None,
+                             wl.hca_count[:nseq] if hca else None, wl.scale)
+
+    with oracle.threads():
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        path()
+        dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    path()
+    dt1 = time.perf_counter() - t0
     scores = int(wl.seq_len[:nseq].sum()) * wl.T
-    return {"value": scores / dt, "unit": "scores/s", "cores": 1, "kind": "oracle",
+    return {"value": scores / dt, "unit": "scores/s", "cores": threads, "kind": "oracle",
             "sample": f"whole path (score, gate, top-k, attention) of sequences 0..{nseq - 1} of "
-                      f"{wl.B}, {scores} scores, {dt:.1f} s single-threaded",
-            "decode_tokens_per_s": nseq * wl.T / dt}
+                      f"{wl.B}, {scores} scores: {dt:.2f} s on {threads} threads, "
+                      f"{dt1:.2f} s on one",
+            "nproc": os.cpu_count(), "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "value_1_thread": scores / dt1,
+            "decode_tokens_per_s": nseq * wl.T / dt,
+            "decode_tokens_per_s_1_thread": nseq * wl.T / dt1}
+
+
+def cpu_burst_prefix(wl, prefix_all: int = 2048, prefix_one: int = 256):
+    """The CPU reference's tau-burst score (max over the 64 positions) of every
+    sequence against a prefix of the shared key set: `prefix_all` entries on all
+    cores, `prefix_one` on one thread; scores/s (a score = one (position, entry)
+    pair), labelled as prefix measurements."""
+    from oracle import oracle
+
+    def run(n):
+        B = wl.B
+        return oracle.index_score(wl.keys[:n], np.zeros(B, np.int64), np.full(B, n, np.int32),
+                                  np.arange(B, dtype=np.int64) * n, wl.q, wl.w, wl.bias,
+                                  reduce_max=True, want_prob=False)
+
+    with oracle.threads():
+        threads = oracle.max_threads()
+        t0 = time.perf_counter()
+        run(prefix_all)
+        dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    run(prefix_one)
+    dt1 = time.perf_counter() - t0
+    per = wl.B * wl.T
+    return {"value": per * prefix_all / dt, "unit": "scores/s", "cores": threads,
+            "kind": "oracle", "value_1_thread": per * prefix_one / dt1,
+            "sample": f"prefix measurement: score + max over {wl.T} positions of {wl.B} "
+                      f"sequences against the first {prefix_all} shared entries on {threads} "
+                      f"threads ({dt:.2f} s), the first {prefix_one} on one ({dt1:.2f} s)"}
+
+
+def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, nbytes: int = 1 << 30):
+    """Ceilings measured in this run by libceiling.so (the best over a few grid sizes):
+    a 1 GiB streaming read, a 1 GiB copy (read + write bytes counted), and a gather
+    of `gather_rows` random rows of `row_bytes` (the attention launch's row count and
+    row size) from a 4 GiB pool, rotating over 24 index lists; GB/s."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(REPO, "lookahead_sparse_kv_amd", "libceiling.so"))
+    P, L, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ceiling_read.argtypes = [P, L, I, P, P]
+    lib.ceiling_copy.argtypes = [P, P, L, I, P]
+    lib.ceiling_gather.argtypes = [P, P, L, L, I, P, P]
+    st = ctypes.c_void_p(stream.cuda_stream)
+    a = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+
+    def ok(rc):
+        assert rc == 0, f"ceiling kernel launch failed ({rc})"
+
+    def best(fn, launches, grids):
+        return min(timed_graph(torch, stream, capture(torch, stream, [lambda g=g: fn(g)] * launches),
+                               launches) for g in grids)
+    t_read = best(lambda g: ok(lib.ceiling_read(a.data_ptr(), nbytes, g, sink.data_ptr(), st)), 4,
+                  (1024, 2048, 4096, 8192))
+    t_copy = best(lambda g: ok(lib.ceiling_copy(a.data_ptr(), b.data_ptr(), nbytes, g, st)), 4,
+                  (1024, 2048, 4096, 8192))
+    del a, b
+    pool_rows = (4 << 30) // row_bytes
+    pool = torch.empty(pool_rows * row_bytes // 4, dtype=torch.int32, device="cuda").fill_(5)
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    lists = [torch.randperm(pool_rows, device="cuda", generator=gen)[:gather_rows]
+             .to(torch.int32).sort().values for _ in range(24)]
+    t_gather = min(timed_graph(torch, stream, capture(torch, stream, [
+        lambda i=i, g=g: ok(lib.ceiling_gather(pool.data_ptr(), lists[i].data_ptr(), gather_rows,
+                                               row_bytes, g, sink.data_ptr(), st))
+        for i in range(24)]), 24) for g in (256, 512, 1024, 2048))
+    del pool, lists
+    return {"read_GBs": round(nbytes / t_read / 1e9, 1),
+            "copy_GBs": round(2 * nbytes / t_copy / 1e9, 1),
+            "gather_GBs": round(gather_rows * row_bytes / t_gather / 1e9, 1),
+            "gather": f"{gather_rows} random {row_bytes}-byte rows (sorted indices) per launch",
+            "bytes": nbytes}
+
+
+def single_launch_us(torch, stream, fn, intervals: int = 25):
+    """Latency of one call: HIP events around the replay of a one-launch graph
+    (includes the graph launch itself, reported beside as graph_launch_floor for a
+    one-element add), median over `intervals` replays."""
+    g = capture(torch, stream, [fn])
+    res = []
+    for it in range(intervals + 3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        e1.synchronize()
+        if it >= 3:
+            res.append(e0.elapsed_time(e1) * 1e3)
+    return round(statistics.median(res), 2)
+
+
+def burst_leg(torch, lsa, inputs, stream, args):
+    """The tau-burst trigger score on its own workload (16 sequences x 64 positions
+    against one shared set of 65536 entries, 64 heads x 128): matrix-core bound,
+    1.0995 TFLOP per launch; key and query replicas rotate."""
+    from lookahead_sparse_kv_amd.pipeline import DeviceInputs
+    wl = inputs.make_workload("burst_tau64")
+    nrep = 4
+    with torch.cuda.stream(stream):
+        d = DeviceInputs(wl, key_replicas=nrep)
+        qs = [d.q] + [d.q.clone() for _ in range(nrep - 1)]
+        z = torch.empty(d.total_entries, dtype=torch.float32, device="cuda")
+
+        def call(i):
+            lsa.lsa_index_score(d.keys[i % nrep], d.key_row_start, d.seq_len, d.entry_start,
+                                d.max_len, qs[i % nrep], d.w, d.bias, reduce_max=True, z_out=z)
+        call(0)
+        torch.cuda.synchronize()
+        r = args.kernel_reps or 8
+        t = timed_graph(torch, stream, capture(torch, stream, [lambda i=i: call(i)
+                                                               for i in range(r)]), r)
+    flops = 2.0 * wl.B * wl.T * int(wl.seq_len[0]) * wl.H * wl.D
+    del d, qs, z
+    return wl, t, flops
 
 
 def main():
@@ -343,6 +480,20 @@ def main():
                      statistics.median(both))
             del pool, hot, win
 
+        # single-call latency: one-launch graphs (graph launch included)
+        floor_t = torch.zeros(1, device="cuda")
+        latency = {"graph_launch_floor": single_launch_us(torch, stream, lambda: floor_t.add_(1)),
+                   "index_score": single_launch_us(torch, stream, p.score),
+                   "select_compact": single_launch_us(torch, stream, p.select),
+                   "topk": single_launch_us(torch, stream, p.topk),
+                   "sparse_attend": single_launch_us(torch, stream, p.attend),
+                   "step": single_launch_us(torch, stream, p.step)}
+        hbm = measured_hbm(torch, stream, att_rows, wl.Dl * wl.latent.itemsize)
+    burst = None
+    if wl.T == 1:
+        # the tau-burst trigger score on its own workload, beside the decode step
+        burst = burst_leg(torch, lsa, inputs, stream, args)
+
     torch.cuda.synchronize()
     counts = p.cand_count.cpu().numpy()
     scores_per_step = int(wl.seq_len.sum()) * wl.T
@@ -362,8 +513,17 @@ def main():
 
     def roof(bound, alg, t, peak, unit, traffic):
         ach = alg / t / (1e9 if unit == "GB/s" else 1e12)
-        return {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
-                "frac": round(ach / peak, 4), "traffic": traffic}
+        r = {"bound": bound, "achieved": round(ach, 1), "peak": peak, "unit": unit,
+             "frac": round(ach / peak, 4), "traffic": traffic}
+        if unit == "GB/s":   # against the ceilings measured in this run, too
+            r["frac_of_measured_read"] = round(ach / hbm["read_GBs"], 4)
+            r["frac_of_measured_copy"] = round(ach / hbm["copy_GBs"], 4)
+        return r
+
+    def gather_roof(r):
+        """attention reads gathered rows: also rate it against the measured gather"""
+        r["frac_of_measured_gather"] = round(r["achieved"] / hbm["gather_GBs"], 4)
+        return r
 
     if wl.T == 1:
         roofline = roof("hbm", score_bytes, t_score, HBM_PEAK_GBS, "GB/s",
@@ -375,6 +535,7 @@ def main():
     roof_att = roof("hbm", att_alg_bytes, t_attend, HBM_PEAK_GBS, "GB/s",
                     None if ta is None else ta + (tc or 0.0))
     roof_att["mfma_frac"] = round(att_flops / t_attend / 1e12 / BF16_PEAK_TFLOPS, 4)
+    gather_roof(roof_att)
 
     line = {
         "metric": METRIC,
@@ -416,7 +577,17 @@ def main():
             "hbm", union3_bytes, t_union3f, HBM_PEAK_GBS, "GB/s",
             read_traffic("score_union", args.workload, "score.hip")),
         "cpu_baseline": None,
+        "hbm_measured": hbm,
+        "latency_us": latency,
     }
+    if burst is not None:
+        bwl, t_b, b_flops = burst
+        line["kernels_us"]["index_score_burst_tau64"] = round(t_b * 1e6, 2)
+        line["roofline_burst"] = roof("mfma", b_flops, t_b, BF16_PEAK_TFLOPS, "TFLOP/s",
+                                      read_traffic("score_burst", "burst_tau64", "score.hip"))
+        line["roofline_burst"]["workload"] = (
+            f"burst_tau64: {bwl.B} sequences x {bwl.T} positions against one shared set of "
+            f"{int(bwl.seq_len[0])} entries, {bwl.H} heads x {bwl.D} bf16")
     t_e = enc["t"]
     line["kernels_us"]["query_encode"] = round(t_e * 1e6, 2)
     line["kernels_us"]["query_encode_torch_mm"] = round(enc["t_lib"] * 1e6, 2)
@@ -446,6 +617,8 @@ def main():
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seqs)
+        line["cpu_baseline"]["burst_prefix"] = cpu_burst_prefix(
+            burst[0] if burst is not None else wl)
     print(json.dumps(line))
 
 

@@ -1,4 +1,5 @@
-"""Compile the HIP sources under csrc/ into liblsa.so (gfx950 only).
+"""Compile the HIP sources under csrc/ into liblsa.so (gfx950 only), and the
+benchmark's measurement kernels (csrc/ceiling.hip) into libceiling.so.
 
 Run as `python -m lookahead_sparse_kv_amd.build` or through
 __graft_entry__.build().  Every call recompiles.
@@ -14,6 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblsa.so")
+CEILING_LIB = os.path.join(HERE, "libceiling.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
@@ -50,18 +52,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + ["ceiling.hip"]
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

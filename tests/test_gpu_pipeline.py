@@ -1,9 +1,11 @@
 """End-to-end parity of the four-call pipeline on the workloads the benchmark times.
 
-Small workloads are compared in full.  At the full 500K / burst / ragged sizes
-the reference scores a sample of entries one by one, the gate and top-k are
-checked through properties that hold at any size, and attention is compared
-on sampled (sequence, position) pairs with indices both sides receive.
+Every workload is compared in full against the reference: every logit, every
+kept set and every top-k set (equal outside the 1e-3 bands).  At the full
+500K / burst / ragged sizes the reference runs on all host cores (its OpenMP
+build), and the pipeline's own attention output is compared with the
+reference attention over the pipeline's own top-k: for every sequence at
+500K and in the ragged mix, at four positions of every sequence of the burst.
 """
 import numpy as np
 import pytest
@@ -66,20 +68,9 @@ def test_pipeline_full_parity(ref, name):
     check_attention(_out64(host(out)), orf, host(lse), lr)
 
 
-def _sampled_scores(ref, wl, g, rng, per_seq):
-    """Reference scores of per_seq sampled entries of every sequence (max over positions)."""
-    for b in range(wl.B):
-        S = int(wl.seq_len[b])
-        s = np.sort(rng.choice(S, size=min(per_seq, S), replace=False))
-        rows = wl.keys[int(wl.key_row_start[b]) + s]
-        zr, _ = ref.index_score(rows, np.zeros(1, np.int64), np.array([len(s)], np.int32),
-                                np.zeros(1, np.int64), wl.q[b:b + 1], wl.w[b:b + 1], wl.bias,
-                                reduce_max=True, want_prob=False)
-        es = int(wl.entry_start[b])
-        check_scores(g["z"][es + s], zr, g["prob"][es + s])
-
-
 def _gate_and_topk_properties(wl, g):
+    """The GPU's candidate list is exactly the gate of its own logits, and its top-k
+    is a valid top-k of them (both hold bit for bit at any size)."""
     for b in range(wl.B):
         es, S = int(wl.entry_start[b]), int(wl.seq_len[b])
         zb = g["z"][es:es + S]
@@ -89,89 +80,93 @@ def _gate_and_topk_properties(wl, g):
         check_topk_properties(g["topk"][b, :g["tcnt"][b]], want, zb, wl.k)
 
 
-def _attention_on_given_indices(ref, wl, d, p, rng, pairs):
-    """Run the benchmark's attention launch on indices both sides receive; compare sampled (b,t)."""
-    B, k = wl.B, wl.k
-    idx = np.full((B, k), -1, np.int32)
-    cnt = np.zeros(B, np.int32)
-    for b in range(B):
-        S = int(wl.seq_len[b])
-        pool = np.flatnonzero(wl.planted[int(wl.key_row_start[b]):int(wl.key_row_start[b]) + S])
-        if len(pool) < k:
-            pool = np.arange(S)
-        c = min(k, len(pool))
-        idx[b, :c] = np.sort(rng.choice(pool, size=c, replace=False))
-        cnt[b] = c
-    out = torch.empty_like(p.out)
-    lse = torch.empty_like(p.lse)
-    lsa.lsa_sparse_attend(d.qa, d.latent[0], d.latent_row_start, torch.from_numpy(idx).cuda(),
-                          torch.from_numpy(cnt).cuda(), k, out, hca=d.hca[0],
-                          hca_row_start=d.hca_row_start, hca_count=d.hca_count,
-                          max_hca=d.max_hca, scale=wl.scale, lse=lse, workspace=p.ws_attend)
-    torch.cuda.synchronize()
-    og, lg = _out64(host(out)), host(lse)
+def _full_set_parity(ref, wl, g):
+    """Every logit, every kept set and every top-k set of the batch against the
+    reference (its OpenMP build; bit-identical to the single-threaded one):
+    sets equal outside the 1e-3 bands around the gate and the k-th key."""
+    with ref.threads():
+        zr, _ = ref.index_score(wl.keys, wl.key_row_start, wl.seq_len, wl.entry_start, wl.q,
+                                wl.w, wl.bias, reduce_max=True, want_prob=False)
+        cr, ccr = ref.select(zr, wl.entry_start, wl.seq_len)
+        tr, tcr = ref.topk(zr, wl.entry_start, wl.seq_len, cr, ccr, wl.k)
+    n = int(wl.entry_start[-1]) + int(wl.seq_len[-1])
+    check_scores(g["z"][:n], zr[:n], g["prob"][:n])
+    diff_sel = diff_top = 0
+    for b in range(wl.B):
+        es, S = int(wl.entry_start[b]), int(wl.seq_len[b])
+        cg, cref = g["cand"][es:es + g["cnt"][b]], cr[es:es + ccr[b]]
+        check_selection(cg, cref, zr[es:es + S])
+        tg, tref = g["topk"][b, :g["tcnt"][b]], tr[b, :tcr[b]]
+        check_topk(tg, tref, zr[es:es + S], wl.k, g["cnt"][b])
+        diff_sel += len(set(cg.tolist()) ^ set(cref.tolist()))
+        diff_top += len(set(tg.tolist()) ^ set(tref.tolist()))
+    announce(f"{wl.name}: {wl.B} sequences, kept-set differences inside the band {diff_sel}, "
+             f"top-k differences inside the bands {diff_top}")
+    return tr, tcr
+
+
+def _attention_on_own_topk(ref, wl, g, pairs=None):
+    """The pipeline's attention output against the reference attention over the
+    pipeline's own top-k (so a set difference inside the bands cannot confound
+    it): every (sequence, position) when pairs is None, else the listed ones."""
+    og, lg = _out64(g["out"]), g["lse"]
+    if pairs is None:
+        with ref.threads():
+            orf, lr = ref.sparse_attend(wl.qa, wl.latent, wl.latent_row_start, g["topk"],
+                                        g["tcnt"], wl.k, wl.hca, wl.hca_row_start, wl.hca_count,
+                                        wl.scale)
+        return check_attention(og, orf, lg, lr)
+    worst = 0.0
     for b, t in pairs:
-        qa = wl.qa[b:b + 1, t:t + 1]
         hca = wl.hca
-        orf, lr = ref.sparse_attend(qa, wl.latent, wl.latent_row_start[b:b + 1], idx[b:b + 1],
-                                    cnt[b:b + 1], k, hca,
-                                    None if hca is None else wl.hca_row_start[b:b + 1],
-                                    None if hca is None else wl.hca_count[b:b + 1], wl.scale)
-        check_attention(og[b:b + 1, t:t + 1], orf, lg[b:b + 1, t:t + 1], lr)
+        with ref.threads():
+            orf, lr = ref.sparse_attend(wl.qa[b:b + 1, t:t + 1], wl.latent,
+                                        wl.latent_row_start[b:b + 1], g["topk"][b:b + 1],
+                                        g["tcnt"][b:b + 1], wl.k, hca,
+                                        None if hca is None else wl.hca_row_start[b:b + 1],
+                                        None if hca is None else wl.hca_count[b:b + 1], wl.scale)
+        worst = max(worst, check_attention(og[b:b + 1, t:t + 1], orf, lg[b:b + 1, t:t + 1], lr))
+    return worst
 
 
 def test_pipeline_decode_500k(ref):
     wl = inputs.make_workload("decode_500k")
     announce("pipeline decode_500k full size")
     d, p, g = _run(wl)
-    rng = np.random.default_rng(1)
-    # sequence 0 in full against the reference, all sequences sampled
-    S0 = int(wl.seq_len[0])
-    z0, _ = ref.index_score(wl.keys[:S0], np.zeros(1, np.int64), wl.seq_len[:1],
-                            np.zeros(1, np.int64), wl.q[:1], wl.w[:1], wl.bias, reduce_max=True,
-                            want_prob=False)
-    check_scores(g["z"][:S0], z0)
-    c0, n0 = ref.select(z0, np.zeros(1, np.int64), wl.seq_len[:1])
-    t0, tn0 = ref.topk(z0, np.zeros(1, np.int64), wl.seq_len[:1], c0, n0, wl.k)
-    check_selection(g["cand"][:g["cnt"][0]], c0[:n0[0]], z0)
-    check_topk(g["topk"][0, :g["tcnt"][0]], t0[0, :tn0[0]], z0, wl.k, g["cnt"][0])
-    _sampled_scores(ref, wl, g, rng, 4000)
     _gate_and_topk_properties(wl, g)
     assert np.all(g["tcnt"] == wl.k)
-    announce("attend decode_500k on given indices")
-    _attention_on_given_indices(ref, wl, d, p, rng, [(0, 0), (5, 0), (7, 0)])
+    announce("decode_500k: reference over all 8 sequences")
+    _full_set_parity(ref, wl, g)
+    rel = _attention_on_own_topk(ref, wl, g)
+    announce(f"decode_500k: attention over the pipeline's top-k, max row rel err {rel:.2e}")
 
 
+@pytest.mark.timeout(1200)
 def test_pipeline_burst(ref):
     wl = inputs.make_workload("burst_tau64")
     announce("pipeline burst_tau64 full size")
     d, p, g = _run(wl)
-    rng = np.random.default_rng(2)
-    # sampled entries: the reference max over 64 positions of the shared keys
-    s = np.sort(rng.choice(65536, size=192, replace=False))
-    rows = wl.keys[s]
-    n = len(s)
-    m, _ = ref.index_score(rows, np.zeros(wl.B, np.int64), np.full(wl.B, n, np.int32),
-                           np.arange(wl.B, dtype=np.int64) * n, wl.q, wl.w, wl.bias,
-                           reduce_max=True, want_prob=False)
-    for b in range(wl.B):
-        check_scores(g["z"][int(wl.entry_start[b]) + s], m[b * n:(b + 1) * n])
     _gate_and_topk_properties(wl, g)
     frac = g["cnt"] / 65536.0
     assert np.all((frac > 0.05) & (frac < 0.3)), frac
-    announce("attend burst on given indices")
-    _attention_on_given_indices(ref, wl, d, p, rng, [(0, 0), (0, 63), (9, 17), (15, 40)])
+    announce("burst_tau64: reference max over 64 positions, all 16 sequences (1.1 TFLOP)")
+    _full_set_parity(ref, wl, g)
+    rng = np.random.default_rng(2)
+    pairs = [(b, int(t)) for b in range(wl.B) for t in rng.choice(wl.T, size=4, replace=False)]
+    rel = _attention_on_own_topk(ref, wl, g, pairs)
+    announce(f"burst_tau64: attention at {len(pairs)} (sequence, position) pairs, "
+             f"max row rel err {rel:.2e}")
 
 
 def test_pipeline_ragged(ref):
     wl = inputs.make_workload("ragged_mix")
     announce("pipeline ragged_mix full size")
     d, p, g = _run(wl)
-    rng = np.random.default_rng(3)
-    _sampled_scores(ref, wl, g, rng, 1500)
     _gate_and_topk_properties(wl, g)
-    announce("attend ragged on given indices")
-    _attention_on_given_indices(ref, wl, d, p, rng, [(0, 0), (13, 0), (31, 0)])
+    announce("ragged_mix: reference over all 32 sequences")
+    _full_set_parity(ref, wl, g)
+    rel = _attention_on_own_topk(ref, wl, g)
+    announce(f"ragged_mix: attention over the pipeline's top-k, max row rel err {rel:.2e}")
 
 
 def test_pipeline_is_deterministic():
