@@ -19,22 +19,17 @@ Recipe (all draws from numpy PCG64 streams spawned from one seed):
     deviations; the rest are pure noise keys;
   * q ~ N(0, 1/d) per element (so a noise dot product is ~N(0,1)), gate
     weights w ~ U(0,1);
-  * the indexer bias is a per-workload constant stored in
-    tests/golden/workload_bias.json (written offline from the CPU reference by
-    tests/golden/make_workload_bias.py); it is an input, like q and w;
+  * the indexer bias is a per-workload constant (WORKLOAD_BIAS below); it is an
+    input, like q and w;
   * bf16 tensors are drawn in fp32 and rounded to nearest-even.
 """
 from __future__ import annotations
 
-import json
-import os
 from dataclasses import dataclass, field
 from typing import Optional
 
 import numpy as np
 
-_REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-BIAS_TABLE = os.path.join(_REPO, "tests", "golden", "workload_bias.json")
 
 TOKENS_PER_ENTRY = 4      # compressed KV entries: 4 tokens each
 HCA_RATIO = 128           # heavily compressed attention: 128 tokens per entry
@@ -112,13 +107,26 @@ DEFAULT_SEED = {"tiny": 11, "decode_128k": 22, "decode_500k": 33, "burst_tau64":
                 "ragged_mix": 55}
 
 
+# Indexer bias of each workload at its default seed.  The values are placed in
+# the widest gap between neighbouring scores near the wanted kept fraction
+# (13.5 % on average, 10 % at 500K tokens; 2 % of noise entries for the planted
+# workloads) by tests/golden/make_workload_bias.py, which scores the drawn keys
+# with the CPU reference; that script writes them to tests/golden/
+# workload_bias.json and a CPU test checks that this table equals that file.
+WORKLOAD_BIAS = {
+    "burst_tau64:44": -27.134510040283203,
+    "decode_128k:22": -18.943151473999023,
+    "decode_500k:33": -19.675514221191406,
+    "ragged_mix:55": -19.771467208862305,
+    "tiny:11": -1.6793327331542969,
+}
+
+
 def load_bias(name: str, seed: int) -> float:
-    with open(BIAS_TABLE) as f:
-        table = json.load(f)
     key = f"{name}:{seed}"
-    if key not in table:
-        raise KeyError(f"no stored bias for workload {key}; run tests/golden/make_workload_bias.py")
-    return float(table[key]["bias"])
+    if key not in WORKLOAD_BIAS:
+        raise KeyError(f"no stored bias for workload {key}; pass bias= explicitly")
+    return WORKLOAD_BIAS[key]
 
 
 def _normal(rng, shape, std=1.0) -> np.ndarray:

@@ -1,4 +1,6 @@
-"""Write tests/golden/workload_bias.json: the indexer bias of each synthetic workload.
+"""Write tests/golden/workload_bias.json: the indexer bias of each synthetic workload
+(the generator lookahead_sparse_kv_amd/inputs.py carries the same values in
+WORKLOAD_BIAS; a CPU test checks the two agree).
 
 The bias is an input of the score (a scalar per indexer).  It is chosen so that
 each workload keeps about the fraction of entries the pages quote (13.5 % on
@@ -63,18 +65,21 @@ def bias_for(name: str, seed: int) -> dict:
     return {"bias": bias, "rule": how, "seconds": round(time.time() - t0, 1)}
 
 
+TABLE = os.path.join(HERE, "workload_bias.json")
+
+
 def main(argv):
     names = argv[1:] or list(inputs.CONFIGS)
     table = {}
-    if os.path.exists(inputs.BIAS_TABLE):
-        with open(inputs.BIAS_TABLE) as f:
+    if os.path.exists(TABLE):
+        with open(TABLE) as f:
             table = json.load(f)
     for name in names:
         seed = inputs.DEFAULT_SEED[name]
         entry = bias_for(name, seed)
         table[f"{name}:{seed}"] = entry
         print(name, seed, entry, flush=True)
-        with open(inputs.BIAS_TABLE, "w") as f:
+        with open(TABLE, "w") as f:
             json.dump(table, f, indent=1, sort_keys=True)
             f.write("\n")
 

@@ -1,7 +1,8 @@
 """The synthetic workloads realise the shapes and selection fractions they are meant to have.
 
 Fractions are measured with the CPU reference on the drawn inputs, so these
-tests also pin the stored bias table (tests/golden/workload_bias.json)."""
+tests also pin the stored bias table (tests/golden/workload_bias.json) and its copy in
+inputs.WORKLOAD_BIAS."""
 import numpy as np
 import pytest
 
@@ -71,3 +72,12 @@ def test_tiny_attention_side():
     wl = inputs.make_workload("tiny")
     assert wl.qa.shape == (1, 1, 8, 64) and wl.latent.shape == (1024, 64)
     assert wl.qa.dtype == np.float32 and wl.hca is None and wl.k == 64
+
+
+def test_embedded_bias_table_equals_the_golden_file():
+    """inputs.WORKLOAD_BIAS is the table tests/golden/make_workload_bias.py writes."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "workload_bias.json")
+    table = json.load(open(path))
+    assert {k: float(v["bias"]) for k, v in table.items()} == inputs.WORKLOAD_BIAS
