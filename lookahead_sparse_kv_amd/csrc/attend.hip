@@ -280,17 +280,30 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             sacc[0] = acc4[0] + acc4[2];
             sacc[1] = acc4[1] + acc4[3];
         }
-        // this lane holds query row 16w + n16 against chunk rows 16rt + 4g + v
+        // this lane holds query row 16w + n16 against chunk rows 16rt + 4g + v.
+        // A full chunk (every chunk but a split's last) needs no row mask, and its
+        // logits are finite, so neither the mask nor the -inf test below runs.
+        const bool full = r0 + kChunk <= re;
         float x[2][4];
         bool over = false;
+        if (full) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const bool valid = r0 + 16 * rt + 4 * g + v < re;
-                x[rt][v] = valid ? sacc[rt][v] * scale_log2 : -INFINITY;
-                over = over || x[rt][v] > m_ref + kRescaleSlack;
-            }
+                for (int v = 0; v < 4; ++v) {
+                    x[rt][v] = sacc[rt][v] * scale_log2;
+                    over = over || x[rt][v] > m_ref + kRescaleSlack;
+                }
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bool valid = r0 + 16 * rt + 4 * g + v < re;
+                    x[rt][v] = valid ? sacc[rt][v] * scale_log2 : -INFINITY;
+                    over = over || x[rt][v] > m_ref + kRescaleSlack;
+                }
+        }
         // Lazy rescale: the running max stands unless some logit of the chunk
         // exceeds it by more than kRescaleSlack (always on the first chunk, as
         // -inf + slack = -inf), so p <= 2^kRescaleSlack.  Rare: the row maxima are
@@ -314,8 +327,9 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             bf16x4 p4;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const bf16 p = (bf16)(x[rt][v] == -INFINITY ? 0.0f
-                                                            : __builtin_amdgcn_exp2f(x[rt][v] - m_ref));
+                // after the rescale step m_ref is finite whenever the chunk has a row
+                const bf16 p = (bf16)(full || x[rt][v] != -INFINITY
+                                          ? __builtin_amdgcn_exp2f(x[rt][v] - m_ref) : 0.0f);
                 p4[v] = p;
                 l_part += (float)p;                 // the sums use the rounded P that P C uses
             }

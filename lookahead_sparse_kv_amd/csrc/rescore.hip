@@ -55,44 +55,56 @@ __global__ __launch_bounds__(256) void k_rescore_mfma(
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int64_t S = seq_len[b];
-    const int64_t C = min(min((int64_t)cand_count[b], max_cand), S);
-    // Groups of the sequence's candidate list are dealt to its waves round robin.
-    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
-    const int64_t nw = (int64_t)gridDim.x * 4;
-    const int64_t G = (C + 15) / 16;
-    if ((int64_t)blockIdx.x * 4 >= G) return;    // no wave of this workgroup has a group
-    // The sequence's queries go to LDS once per workgroup (every wave needs all
-    // of them; a per-wave copy from memory would move as many bytes as the keys).
-    {
-        const bf16x8* qg = reinterpret_cast<const bf16x8*>(q + (int64_t)b * H * D);
-        for (int e = threadIdx.x; e < H * D / 8; e += 256)
-            reinterpret_cast<bf16x8*>(sq)[e] = qg[e];
-    }
-    __syncthreads();
-    if (gw >= G) return;
-    const int ngroups = (int)min((G - gw + nw - 1) / nw, (int64_t)GPW);
     const int n16 = lane & 15;
     const int g = lane >> 4;
+    // Groups of 16 list positions are dealt to the sequence's waves round robin.
+    // The list length is on the device, so the queries and this wave's candidate
+    // indices are loaded speculatively, straight into LDS, together with the
+    // counts: positions up to the most the grid can hold (from the host bound
+    // max_cand), the index buffer ranged to the sequence's S_b slots, so no
+    // load leaves the list's storage.  The key copies then follow one round
+    // trip later.
+    const int64_t gw = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t nw = (int64_t)gridDim.x * 4;
+    const int64_t G_grid = (max_cand + 15) / 16;
+    const int ng_spec = (int)max((int64_t)0, min((G_grid - gw + nw - 1) / nw, (int64_t)GPW));
+    const int64_t S = seq_len[b];
     const int64_t eo = entry_start[b];
-    const int32_t* cl = cand_idx + eo;
-
-    // Stage this wave's candidate indices (group i at myidx[16 i ..]); positions
-    // past the list repeat its last candidate (never written back).
+    {
+        const __amdgpu_buffer_rsrc_t ir = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(cand_idx + eo), (short)0, (int)min(S * 4, (int64_t)0x7fffffff), kBufferWord3);
+        // lane L of copy k4 fills myidx[64 k4 + L]: group i = 4 k4 + L / 16, slot L % 16
 #pragma unroll
-    for (int k4 = 0; k4 < GPW / 4; ++k4) {
-        const int i = g + 4 * k4;
-        if (i < ngroups) {
-            const int64_t p = 16 * (gw + nw * i) + n16;
-            myidx[16 * i + n16] = cl[min(p, C - 1)];
+        for (int k4 = 0; k4 < GPW / 4; ++k4) {
+            if (4 * k4 < ng_spec) {
+                const int i = 4 * k4 + g;
+                const uint32_t pos = (uint32_t)(16 * (gw + nw * i) + n16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ir, (__attribute__((address_space(3))) void*)(myidx + 64 * k4), 4, 4u * pos,
+                    0, 0, 0);
+            }
         }
+        // the sequence's [H][D] queries: 1 KiB per copy, copies dealt to the waves
+        const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(q + (int64_t)b * H * D), (short)0, H * D * 2, kBufferWord3);
+        for (int c = wave; c < (H * D * 2 + 1023) / 1024; c += 4)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                qr, (__attribute__((address_space(3))) void*)(reinterpret_cast<unsigned char*>(sq) + 1024 * c),
+                16, (uint32_t)(1024 * c + 16 * lane), 0, 0, 0);
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the wave's index writes landed
-
+    const int64_t C = min(min((int64_t)cand_count[b], max_cand), S);
+    const int64_t G = (C + 15) / 16;
+    wait_vmcnt<0>();                             // this wave's indices and query copies landed
+    __syncthreads();                             // ... and every wave's queries
+    if (gw >= G) return;
+    const int ngroups = (int)min((G - gw + nw - 1) / nw, (int64_t)GPW);
+    // key rows of the sequence; positions past the list hold no candidate: their
+    // copies read whatever row their stale index names (or nothing, outside the
+    // range) and their logits are never written
     const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(keys + key_row_start[b] * D), (short)0, (int)min(S * D * 2, (int64_t)0x7fffffff),
         kBufferWord3);
+
     // Group i goes to ring slot i % NB.  Copy j of a group moves rows RPI*j ..;
     // lane L fills physical slot L % SLOTS of row r = RPI*j + L/SLOTS.
     auto issue = [&](int i) {
