@@ -292,6 +292,32 @@ def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, nbytes: int = 
             "bytes": nbytes}
 
 
+def measured_mfma(torch, stream, n: int = 8192, reps: int = 8):
+    """The bf16 matrix rate a library GEMM reaches in this run, as a measured
+    ceiling for matrix-core-bound kernels: torch.mm (hipBLASLt) of two n x n bf16
+    matrices with fp32 accumulation, timed over `reps` launches after three
+    untimed ones; TFLOP/s.  Under sustained matrix load the engine clock settles
+    below the 2.4 GHz that the published peak assumes."""
+    with torch.cuda.stream(stream):
+        gen = torch.Generator(device="cuda").manual_seed(3)
+        a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+        b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=gen)
+        c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.mm(a, b, out=c)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            torch.mm(a, b, out=c)
+        e1.record(stream)
+        e1.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b, c
+    return {"bf16_gemm_TFLOPs": round(2.0 * n ** 3 / t / 1e12, 1),
+            "gemm": f"torch.mm {n}x{n}x{n} bf16, fp32 accumulation (hipBLASLt)"}
+
+
 def single_launch_us(torch, stream, fn, intervals: int = 25):
     """Latency of one call: HIP events around the replay of a one-launch graph
     (includes the graph launch itself, reported beside as graph_launch_floor for a
@@ -333,7 +359,7 @@ def burst_leg(torch, lsa, inputs, stream, args):
                                                                for i in range(r)]), r)
     flops = 2.0 * wl.B * wl.T * int(wl.seq_len[0]) * wl.H * wl.D
     del d, qs, z
-    return wl, t, flops
+    return wl, t, flops, measured_mfma(torch, stream)
 
 
 def main():
@@ -581,10 +607,13 @@ def main():
         "latency_us": latency,
     }
     if burst is not None:
-        bwl, t_b, b_flops = burst
+        bwl, t_b, b_flops, mfma_meas = burst
         line["kernels_us"]["index_score_burst_tau64"] = round(t_b * 1e6, 2)
         line["roofline_burst"] = roof("mfma", b_flops, t_b, BF16_PEAK_TFLOPS, "TFLOP/s",
                                       read_traffic("score_burst", "burst_tau64", "score.hip"))
+        line["roofline_burst"]["frac_of_measured_gemm"] = round(
+            line["roofline_burst"]["achieved"] / mfma_meas["bf16_gemm_TFLOPs"], 4)
+        line["mfma_measured"] = mfma_meas
         line["roofline_burst"]["workload"] = (
             f"burst_tau64: {bwl.B} sequences x {bwl.T} positions against one shared set of "
             f"{int(bwl.seq_len[0])} entries, {bwl.H} heads x {bwl.D} bf16")
