@@ -446,6 +446,12 @@ def main():
             torch, stream, [lambda i=i: p.score(i) for i in range(r)]), r)
         r = reps_for(1e-5)
         t_select = timed_graph(torch, stream, capture(torch, stream, [p.select] * r), r)
+        t_select_z = timed_graph(torch, stream, capture(torch, stream, [p.select_from_logits] * r),
+                                 r)
+        # the floor of this timing method: back-to-back launches of a one-element add
+        floor_e = torch.zeros(1, device="cuda")
+        t_floor = timed_graph(torch, stream, capture(torch, stream, [lambda: floor_e.add_(1)] * r),
+                              r)
         t_topk = timed_graph(torch, stream, capture(torch, stream, [p.topk] * r), r)
         r = reps_for(step_s / 4)
         t_attend = timed_graph(torch, stream, capture(
@@ -582,6 +588,8 @@ def main():
                    "hca_rows_per_seq": wl.max_hca, "parallelism": "single GPU"},
         "kernels_us": {"index_score": round(t_score * 1e6, 2),
                        "select_compact": round(t_select * 1e6, 2),
+                       "select_compact_from_logits": round(t_select_z * 1e6, 2),
+                       "one_element_add_floor": round(t_floor * 1e6, 2),
                        "topk": round(t_topk * 1e6, 2),
                        "sparse_attend": round(t_attend * 1e6, 2),
                        "index_rescore": round(t_rescore * 1e6, 2),

@@ -81,6 +81,12 @@ extern "C" {
 #define LSA_OP_TOPK 2
 #define LSA_OP_ATTEND 3
 
+/* Gate bits: one uint16 word per group of 16 consecutive entries of a
+ * sequence, bit i for entry 16 j + i of group j.  Sequence b's row starts at
+ * word b * lsa_gate_words(max_len) = b * 8 * ceil(max_len / 128), so every
+ * row is 16-byte aligned; words past ceil(S_b / 16) are not written. */
+static inline int64_t lsa_gate_words(int64_t max_len) { return (max_len + 127) / 128 * 8; }
+
 /* Lookahead index score (section 2.1 "Scoring Mechanism"; the query/key
  * interaction is a dot product per section 5 "Architectural Constraints").
  * This library's instance of the head-fused gated score:
@@ -102,13 +108,22 @@ extern "C" {
  *                   and receives max(z_out, m) (a NaN on either side yields
  *                   the other); prob_out, if given, holds its sigmoid.
  *   prob_out may be NULL.  Accumulation is fp32; bf16 products are exact.
+ *   gate_bits, if not NULL (16-byte aligned, B rows of lsa_gate_words
+ *              (max_len) words): the gate of section 2.1 "Dynamic Fetching"
+ *              taken in the same launch on the value written to z_out --
+ *              bit i of word j of row b is set iff entry 16 j + i < S_b and
+ *              that logit >= gate_threshold (a NaN never passes).  It needs
+ *              T = 1 or reduce_max != 0 (one logit per entry); with
+ *              reduce_max = 2 the bits are those of the combined value.
+ *              lsa_select_compact then compacts from the bits alone.
  * Envelope: B, T, H, D >= 1; the bf16 matrix-core path takes H <= 64 and
  * D in {64, 128}; other shapes (and fp32) use the vector path, which needs
  * T*H*(D+1) <= 16384.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
 int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
                     const int32_t* seq_len, const int64_t* entry_start, int B, int T, int H,
                     int D, int64_t max_len, const void* q, const float* w, float bias,
-                    int reduce_max, float* z_out, float* prob_out, void* stream);
+                    int reduce_max, float* z_out, float* prob_out, uint16_t* gate_bits,
+                    float gate_threshold, void* stream);
 
 /* OR-union of several indexers' scores in one call (section 2.4 "Optimal
  * Configuration": the indexers of three intermediate layers, united by OR; an
@@ -117,7 +132,9 @@ int lsa_index_score(const void* keys, int dtype, const int64_t* key_row_start,
  * q[l], w[l] and bias[l], laid out as for lsa_index_score; all share the
  * sequence layout (key_row_start, seq_len, entry_start), dtype, B, T, H, D.
  *   z_out[entry_start[b] + s] = max over l and t of z_l[b,t,s];
- *   prob_out, if not NULL, holds its sigmoid.
+ *   prob_out, if not NULL, holds its sigmoid; gate_bits, if not NULL, the
+ *   gate of that union against gate_threshold, laid out as for
+ *   lsa_index_score.
  * keys, q, w and bias are HOST arrays of n_idx entries; the pointers in
  * keys, q and w are device pointers.  The bf16 matrix-core shapes with T = 1
  * (H <= 64, D in {64, 128}) stream every indexer's keys in one launch and
@@ -131,7 +148,8 @@ int lsa_index_score_union(int n_idx, const void* const* keys, int dtype,
                           const int64_t* key_row_start, const int32_t* seq_len,
                           const int64_t* entry_start, int B, int T, int H, int D,
                           int64_t max_len, const void* const* q, const float* const* w,
-                          const float* bias, float* z_out, float* prob_out, void* stream);
+                          const float* bias, float* z_out, float* prob_out,
+                          uint16_t* gate_bits, float gate_threshold, void* stream);
 
 /* Native re-score of the kept subset (section 2.1 "Tiered Selection": the
  * backbone's native Lightning Indexer takes the fine-grained top-k inside the
@@ -184,21 +202,29 @@ int lsa_query_encode(const void* h, int M, int d_model, int rank, int H, int D,
  * fixed count.  I >= 0.5 holds exactly when z >= 0, so the gate is taken on
  * the fp32 logit: candidate s of sequence b iff z[entry_start[b]+s] >=
  * threshold (pass 0.0f for the 0.5 gate; -0.0 passes, NaN never does).
+ *   gate_bits  NULL: the gate is taken on z (two launches: per-tile counts,
+ *              then the ordered scatter).  Otherwise the bits that
+ *              lsa_index_score wrote in its launch for the same z, max_len
+ *              and threshold (16-byte aligned): the kept set is the set bits,
+ *              z is not read (it may be NULL), threshold and the workspace
+ *              are not used (workspace may be NULL), and one launch compacts.
  *   cand_idx   int32, the ascending list of kept s for sequence b written at
  *              cand_idx[entry_start[b] ...]; capacity S_b per sequence.
  *   cand_count int32 [B].
  *   workspace  lsa_workspace_bytes(LSA_OP_SELECT, B, 0, 0, 0, max_len, 0, 0) bytes.
- * Deterministic: the list is in ascending s whatever the launch order.
+ * Deterministic: the list is in ascending s whatever the launch order; both
+ * forms give the same list for bits made from the same logits.
  * Errors: INVALID_ARG, WORKSPACE, HIP. */
-int lsa_select_compact(const float* z, const int64_t* entry_start, const int32_t* seq_len,
-                       int B, int64_t max_len, float threshold, int32_t* cand_idx,
-                       int32_t* cand_count, void* workspace, size_t workspace_bytes,
-                       void* stream);
+int lsa_select_compact(const float* z, const uint16_t* gate_bits, const int64_t* entry_start,
+                       const int32_t* seq_len, int B, int64_t max_len, float threshold,
+                       int32_t* cand_idx, int32_t* cand_count, void* workspace,
+                       size_t workspace_bytes, void* stream);
 
 /* lsa_select_compact without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
- * that forbid hipMalloc).  Same arguments, results and errors as
- * lsa_select_compact, minus the workspace: the per-tile counts live in a
+ * that forbid hipMalloc).  Same arguments, results and errors as the z form
+ * of lsa_select_compact (gate_bits NULL), minus the workspace (the bit form
+ * needs none): the per-tile counts live in a
  * built-in device array of 2^18 int32 (1 MiB per GPU, held until the process
  * ends), so B * ceil(max_len / 2048) must not exceed 262144 (else
  * UNSUPPORTED).  The call allocates nothing.  Calls that overlap on one GPU

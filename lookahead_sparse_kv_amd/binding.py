@@ -53,10 +53,10 @@ def load_library(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     P, I, L, F, Z = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
                      ctypes.c_size_t)
-    lib.lsa_index_score.argtypes = [P, I, P, P, P, I, I, I, I, L, P, P, F, I, P, P, P]
-    lib.lsa_index_score_union.argtypes = [I, P, I, P, P, P, I, I, I, I, L, P, P, P, P, P, P]
+    lib.lsa_index_score.argtypes = [P, I, P, P, P, I, I, I, I, L, P, P, F, I, P, P, P, F, P]
+    lib.lsa_index_score_union.argtypes = [I, P, I, P, P, P, I, I, I, I, L, P, P, P, P, P, P, F, P]
     lib.lsa_index_rescore.argtypes = [P, I, P, P, P, P, P, I, I, I, L, P, P, P, P]
-    lib.lsa_select_compact.argtypes = [P, P, P, I, L, F, P, P, P, Z, P]
+    lib.lsa_select_compact.argtypes = [P, P, P, P, I, L, F, P, P, P, Z, P]
     lib.lsa_select_compact_noalloc.argtypes = [P, P, P, I, L, F, P, P, P]
     lib.lsa_topk.argtypes = [P, P, P, I, L, P, P, I, P, P, I, P, Z, P]
     lib.lsa_fetch_rows.argtypes = [P, L, P, P, P, P, I, L, P, P, P]
@@ -121,12 +121,29 @@ def lsa_version() -> int:
     return int(load_library().lsa_version())
 
 
+def lsa_gate_words(max_len: int) -> int:
+    """uint16 words per sequence row of the gate bits (include/lsa.h)."""
+    return (int(max_len) + 127) // 128 * 8
+
+
+def _gate_buf(gate_bits, B: int, max_len: int):
+    if gate_bits is None:
+        return None
+    _dev(gate_bits, "gate_bits", torch.int16)
+    if gate_bits.numel() < B * lsa_gate_words(max_len):
+        raise ValueError(f"gate_bits needs {B} x {lsa_gate_words(max_len)} int16 words")
+    return gate_bits
+
+
 def lsa_index_score(keys, key_row_start, seq_len, entry_start, max_len: int, q, w, bias: float,
-                    reduce_max=False, z_out=None, prob_out=None, stream=None):
+                    reduce_max=False, z_out=None, prob_out=None, gate_bits=None,
+                    gate_threshold: float = 0.0, stream=None):
     """Score every entry (see include/lsa.h).  q: [B, T, H, D], w: [B, T, H].
 
     reduce_max: False/0 per position, True/1 max over positions, 2 OR-union
-    with the indexers already in z_out."""
+    with the indexers already in z_out.  gate_bits: int16 [B, lsa_gate_words(
+    max_len)] (the words are bit sets), filled with the gate against
+    gate_threshold in the same launch."""
     lib = load_library()
     B, T, H, D = q.shape
     _dev(keys, "keys")
@@ -140,16 +157,18 @@ def lsa_index_score(keys, key_row_start, seq_len, entry_start, max_len: int, q, 
     _dev(z_out, "z_out", torch.float32)
     if prob_out is not None:
         _dev(prob_out, "prob_out", torch.float32)
+    gate_bits = _gate_buf(gate_bits, B, max_len)
     rc = lib.lsa_index_score(_ptr(keys), _dtype_code(keys), _ptr(key_row_start), _ptr(seq_len),
                              _ptr(entry_start), B, T, H, D, int(max_len), _ptr(q), _ptr(w),
                              float(bias), int(reduce_max), _ptr(z_out), _ptr(prob_out),
-                             _stream(stream))
+                             _ptr(gate_bits), float(gate_threshold), _stream(stream))
     _check("lsa_index_score", rc)
     return z_out, prob_out
 
 
 def lsa_index_score_union(keys, key_row_start, seq_len, entry_start, max_len: int, qs, ws,
-                          biases, z_out, prob_out=None, stream=None):
+                          biases, z_out, prob_out=None, gate_bits=None,
+                          gate_threshold: float = 0.0, stream=None):
     """OR-union over indexers (see include/lsa.h): keys, qs, ws and biases are
     sequences with one entry per indexer; q: [B, T, H, D], w: [B, T, H]."""
     lib = load_library()
@@ -176,9 +195,11 @@ def lsa_index_score_union(keys, key_row_start, seq_len, entry_start, max_len: in
     qp = arr(*(q.data_ptr() for q in qs))
     wp = arr(*(w.data_ptr() for w in ws))
     bp = (ctypes.c_float * n)(*(float(b) for b in biases))
+    gate_bits = _gate_buf(gate_bits, B, max_len)
     rc = lib.lsa_index_score_union(n, kp, _dtype_code(keys[0]), _ptr(key_row_start),
                                    _ptr(seq_len), _ptr(entry_start), B, T, H, D, int(max_len), qp,
-                                   wp, bp, _ptr(z_out), _ptr(prob_out), _stream(stream))
+                                   wp, bp, _ptr(z_out), _ptr(prob_out), _ptr(gate_bits),
+                                   float(gate_threshold), _stream(stream))
     _check("lsa_index_score_union", rc)
     return z_out, prob_out
 
@@ -206,15 +227,23 @@ def lsa_index_rescore(keys, key_row_start, seq_len, entry_start, cand_idx, cand_
 
 
 def lsa_select_compact(z, entry_start, seq_len, max_len: int, cand_idx, cand_count, workspace,
-                       threshold: float = 0.0, stream=None):
+                       threshold: float = 0.0, stream=None, gate_bits=None):
+    """Ascending list of kept entries (see include/lsa.h): from the logits z, or,
+    with gate_bits (written by lsa_index_score), from the bits alone (z, the
+    threshold and the workspace are then unused and may be None)."""
     lib = load_library()
-    _dev(z, "z", torch.float32)
+    B = seq_len.numel()
+    if gate_bits is None:
+        _dev(z, "z", torch.float32)
+    else:
+        gate_bits = _gate_buf(gate_bits, B, max_len)
+        if z is not None:
+            _dev(z, "z", torch.float32)
     _dev(cand_idx, "cand_idx", torch.int32)
     _dev(cand_count, "cand_count", torch.int32)
-    B = seq_len.numel()
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.lsa_select_compact(_ptr(z), _ptr(entry_start), _ptr(seq_len), B, int(max_len),
-                                float(threshold), _ptr(cand_idx), _ptr(cand_count),
+    rc = lib.lsa_select_compact(_ptr(z), _ptr(gate_bits), _ptr(entry_start), _ptr(seq_len), B,
+                                int(max_len), float(threshold), _ptr(cand_idx), _ptr(cand_count),
                                 _ptr(workspace), ws_bytes, _stream(stream))
     _check("lsa_select_compact", rc)
     return cand_idx, cand_count

@@ -44,7 +44,8 @@ __global__ __launch_bounds__(256) void k_score_decode(
     const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int H,
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
-    float* __restrict__ z_out, float* __restrict__ prob_out) {
+    float* __restrict__ z_out, float* __restrict__ prob_out, uint16_t* __restrict__ gate_bits,
+    int64_t gstride, float gthr) {
     constexpr int D = 32 * KT;
     constexpr int SLOTS = D / 8;                 // 16-byte slots per key row
     constexpr int RPI = 64 / SLOTS;              // rows per direct-to-LDS instruction
@@ -139,12 +140,19 @@ __global__ __launch_bounds__(256) void k_score_decode(
             for (int v = 0; v < 4; ++v) sacc += wv[mt][v] * relu_bits(acc[mt][v]);
         sacc += __shfl_xor(sacc, 16);
         sacc += __shfl_xor(sacc, 32);
-        const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
-        if (g == 0 && n < last) {
-            float z = sacc + bias;
+        const int64_t grp = gw + nw * (int64_t)i;
+        const int64_t n = 16 * grp + n16;
+        const bool own = g == 0 && n < last;
+        float z = sacc + bias;
+        if (own) {
             if (COMBINE) z = fmaxf(z_out[eo + n], z);   // OR-union with earlier indexers
             z_out[eo + n] = z;
             if (prob_out) prob_out[eo + n] = sigmoidf(z);
+        }
+        // the gate of the group's 16 entries (lanes 0..15), one 16-bit word
+        if (gate_bits) {
+            const uint64_t m = __ballot(own && z >= gthr);
+            if (lane == 0) gate_bits[(int64_t)b * gstride + grp] = (uint16_t)m;
         }
     }
 }
@@ -202,7 +210,7 @@ template <int MT, int KT>
 __global__ __launch_bounds__(256) void k_score_union(
     UnionArgs u, const int64_t* __restrict__ key_row_start, const int32_t* __restrict__ seq_len,
     const int64_t* __restrict__ entry_start, int H, int64_t max_len, float* __restrict__ z_out,
-    float* __restrict__ prob_out) {
+    float* __restrict__ prob_out, uint16_t* __restrict__ gate_bits, int64_t gstride, float gthr) {
     constexpr int D = 32 * KT;
     constexpr int SLOTS = D / 8;
     constexpr int RPI = 64 / SLOTS;
@@ -321,10 +329,18 @@ __global__ __launch_bounds__(256) void k_score_union(
 #pragma unroll
     for (int s8 = 0; s8 < ZS; ++s8) {
         const int i = 4 * s8 + g;
-        const int64_t n = 16 * (gw + nw * (int64_t)i) + n16;
-        if (i < ngroups && n < last) {
+        const int64_t grp = gw + nw * (int64_t)i;
+        const int64_t n = 16 * grp + n16;
+        const bool own = i < ngroups && n < last;
+        if (own) {
             z_out[eo + n] = zmax[s8];
             if (prob_out) prob_out[eo + n] = sigmoidf(zmax[s8]);
+        }
+        // lanes 16 g .. 16 g + 15 hold group i's gate: one 16-bit word each
+        if (gate_bits && 4 * s8 < ngroups) {
+            const uint64_t m = __ballot(own && zmax[s8] >= gthr);
+            if (n16 == 0 && i < ngroups)
+                gate_bits[(int64_t)b * gstride + grp] = (uint16_t)(m >> (16 * g));
         }
     }
 }
@@ -359,7 +375,8 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
     const bf16* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int T, int H,
     int64_t max_len, const bf16* __restrict__ q, const float* __restrict__ w, float bias,
-    int reduce_max, float* __restrict__ z_out, float* __restrict__ prob_out) {
+    int reduce_max, float* __restrict__ z_out, float* __restrict__ prob_out,
+    uint16_t* __restrict__ gate_bits, int64_t gstride, float gthr) {
     constexpr int D = 16 * KS;
     constexpr int CH = D / 8;                 // 16-byte chunks per query row
     constexpr int QCHUNKS = 64 * CH;          // per position (64 head slots)
@@ -487,15 +504,25 @@ __global__ __launch_bounds__(64 * NW, MINB) void k_score_burst(
         }
     }
     wait_vmcnt<0>();                    // no copy lands after the workgroup ends
-    if (reduce_max && g == 0) {
+    if (reduce_max) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-            if (ent[nt] < S) {
+        for (int nt = 0; nt < NT; ++nt) {
+            const bool own = g == 0 && ent[nt] < S;
+            float m = mx[nt];
+            if (own) {
                 // reduce_max == 2: OR-union with the indexers already in z_out
-                const float m = reduce_max == 2 ? fmaxf(z_out[eo + ent[nt]], mx[nt]) : mx[nt];
+                if (reduce_max == 2) m = fmaxf(z_out[eo + ent[nt]], m);
                 z_out[eo + ent[nt]] = m;
                 if (prob_out) prob_out[eo + ent[nt]] = sigmoidf(m);
             }
+            // lanes 0..31 hold two groups of 16 entries: two 16-bit words
+            if (gate_bits) {
+                const uint64_t bits = __ballot(own && m >= gthr);
+                const int64_t grp = (e_blk + wave * EPW + nt * 32) / 16 + (lane >> 4);
+                if ((lane == 0 || lane == 16) && 16 * grp < S)
+                    gate_bits[(int64_t)b * gstride + grp] = (uint16_t)(bits >> lane);
+            }
+        }
     }
 }
 
@@ -506,7 +533,8 @@ __global__ __launch_bounds__(256) void k_score_vector(
     const E* __restrict__ keys, const int64_t* __restrict__ key_row_start,
     const int32_t* __restrict__ seq_len, const int64_t* __restrict__ entry_start, int T, int H,
     int D, int64_t max_len, const E* __restrict__ q, const float* __restrict__ w, float bias,
-    int reduce_max, float* __restrict__ z_out, float* __restrict__ prob_out) {
+    int reduce_max, float* __restrict__ z_out, float* __restrict__ prob_out,
+    uint16_t* __restrict__ gate_bits, int64_t gstride, float gthr) {
     extern __shared__ float smem[];
     float* sq = smem;               // [T*H*D]
     float* sw = smem + T * H * D;   // [T*H]
@@ -517,11 +545,14 @@ __global__ __launch_bounds__(256) void k_score_vector(
     __syncthreads();
     const int64_t S = min((int64_t)seq_len[b], max_len);
     const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= S) return;
-    const E* row = keys + (key_row_start[b] + s) * D;
+    // a wave's 64 entries are four groups of 16; waves past the sequence end stop
+    if (s - (threadIdx.x & 63) >= S) return;
+    const bool live = s < S;
+    const E* row = keys + (key_row_start[b] + (live ? s : 0)) * D;
     const int64_t eo = entry_start[b];
     float m = -INFINITY;
-    for (int t = 0; t < T; ++t) {
+    float zlast = 0.0f;                 // the logit the gate reads
+    if (live) for (int t = 0; t < T; ++t) {
         float u = 0.0f;
         // eight heads per pass over the row: each key element is loaded once per
         // pass, not once per head (head sums still added in head order)
@@ -545,12 +576,22 @@ __global__ __launch_bounds__(256) void k_score_vector(
             const int64_t o = eo * T + (int64_t)t * S + s;
             z_out[o] = z;
             if (prob_out) prob_out[o] = sigmoidf(z);
+            zlast = z;
         }
     }
-    if (reduce_max) {
+    if (reduce_max && live) {
         if (reduce_max == 2) m = fmaxf(z_out[eo + s], m);   // OR-union with earlier indexers
         z_out[eo + s] = m;
         if (prob_out) prob_out[eo + s] = sigmoidf(m);
+        zlast = m;
+    }
+    // (gate bits are only asked for with one position or a reduction)
+    if (gate_bits) {
+        const int l = threadIdx.x & 63;
+        const uint64_t bits = __ballot(live && zlast >= gthr);
+        const int64_t grp = (s - l) / 16 + (l >> 4);
+        if ((l & 15) == 0 && 16 * grp < S)
+            gate_bits[(int64_t)b * gstride + grp] = (uint16_t)(bits >> l);
     }
 }
 
@@ -558,16 +599,16 @@ template <int MT, int KT>
 static void launch_decode(dim3 grid, hipStream_t st, const void* keys, const int64_t* krs,
                           const int32_t* lens, const int64_t* es, int H, int64_t max_len,
                           const void* q, const float* w, float bias, bool combine, float* z,
-                          float* p) {
+                          float* p, uint16_t* gb, int64_t gs, float gthr) {
     // the OR-union mode is its own instantiation: the plain kernel keeps its code
     if (combine)
         hipLaunchKernelGGL((k_score_decode<MT, KT, true>), grid, dim3(256), 0, st,
                            (const bf16*)keys, krs, lens, es, H, max_len, (const bf16*)q, w, bias, z,
-                           p);
+                           p, gb, gs, gthr);
     else
         hipLaunchKernelGGL((k_score_decode<MT, KT, false>), grid, dim3(256), 0, st,
                            (const bf16*)keys, krs, lens, es, H, max_len, (const bf16*)q, w, bias, z,
-                           p);
+                           p, gb, gs, gthr);
 }
 
 }  // namespace lsa
@@ -578,10 +619,15 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
                                const int32_t* seq_len, const int64_t* entry_start, int B, int T,
                                int H, int D, int64_t max_len, const void* q, const float* w,
                                float bias, int reduce_max, float* z_out, float* prob_out,
-                               void* stream) {
+                               uint16_t* gate_bits, float gate_threshold, void* stream) {
     clear_error();
     if (!keys || !key_row_start || !seq_len || !entry_start || !q || !w || !z_out)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: a required pointer is NULL");
+    if (gate_bits && T > 1 && reduce_max == 0)
+        return fail(LSA_ERR_INVALID_ARG,
+                    "lsa_index_score: gate bits need one position or reduce_max (T=%d)", T);
+    if (gate_bits && !aligned16(gate_bits))
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: gate_bits must be 16-byte aligned");
     if (B <= 0 || T <= 0 || H <= 0 || D <= 0 || max_len < 0)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score: B=%d T=%d H=%d D=%d max_len=%lld", B, T,
                     H, D, (long long)max_len);
@@ -605,6 +651,7 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
     if (rc != LSA_OK) return rc;
     if (max_len == 0) return LSA_OK;
     hipStream_t st = (hipStream_t)stream;
+    const int64_t gs = lsa_gate_words(max_len);
 
     if (mfma_shape && T == 1) {
         const int64_t groups = ceil_div(max_len, 16);
@@ -616,7 +663,7 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
         const int MT = H <= 16 ? 1 : (H <= 32 ? 2 : 4);
 #define LSA_DEC(mt, kt)                                                                      \
     launch_decode<mt, kt>(grid, st, keys, key_row_start, seq_len, entry_start, H, max_len, q, \
-                          w, bias, reduce_max == 2, z_out, prob_out)
+                          w, bias, reduce_max == 2, z_out, prob_out, gate_bits, gs, gate_threshold)
         // With one position the [T, S_b] layout and the reduced layout coincide.
         if (D == 128) {
             if (MT == 1) LSA_DEC(1, 4); else if (MT == 2) LSA_DEC(2, 4); else LSA_DEC(4, 4);
@@ -634,12 +681,12 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
             hipLaunchKernelGGL((k_score_burst<8, kBurstWaves, kBurstTiles, kBurstMinBlocks>), grid,
                                dim3(64 * kBurstWaves), 0, st, (const bf16*)keys, key_row_start,
                                seq_len, entry_start, T, H, max_len, (const bf16*)q, w, bias,
-                               reduce_max, z_out, prob_out);
+                               reduce_max, z_out, prob_out, gate_bits, gs, gate_threshold);
         else
             hipLaunchKernelGGL((k_score_burst<4, kBurstWaves, kBurstTiles, kBurstMinBlocks>), grid,
                                dim3(64 * kBurstWaves), 0, st, (const bf16*)keys, key_row_start,
                                seq_len, entry_start, T, H, max_len, (const bf16*)q, w, bias,
-                               reduce_max, z_out, prob_out);
+                               reduce_max, z_out, prob_out, gate_bits, gs, gate_threshold);
         return launch_status("score_burst");
     }
     dim3 grid((unsigned)ceil_div(max_len, 256), (unsigned)B);
@@ -647,11 +694,11 @@ extern "C" int lsa_index_score(const void* keys, int dtype, const int64_t* key_r
     if (dtype == LSA_DTYPE_F32)
         hipLaunchKernelGGL(k_score_vector<float>, grid, dim3(256), shm, st, (const float*)keys,
                            key_row_start, seq_len, entry_start, T, H, D, max_len, (const float*)q,
-                           w, bias, reduce_max, z_out, prob_out);
+                           w, bias, reduce_max, z_out, prob_out, gate_bits, gs, gate_threshold);
     else
         hipLaunchKernelGGL(k_score_vector<bf16>, grid, dim3(256), shm, st, (const bf16*)keys,
                            key_row_start, seq_len, entry_start, T, H, D, max_len, (const bf16*)q,
-                           w, bias, reduce_max, z_out, prob_out);
+                           w, bias, reduce_max, z_out, prob_out, gate_bits, gs, gate_threshold);
     return launch_status("score_vector");
 }
 
@@ -660,7 +707,8 @@ extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dty
                                      const int64_t* entry_start, int B, int T, int H, int D,
                                      int64_t max_len, const void* const* q,
                                      const float* const* w, const float* bias, float* z_out,
-                                     float* prob_out, void* stream) {
+                                     float* prob_out, uint16_t* gate_bits, float gate_threshold,
+                                     void* stream) {
     clear_error();
     if (!keys || !q || !w || !bias)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: a required array is NULL");
@@ -685,7 +733,9 @@ extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dty
             const int rc = lsa_index_score(keys[l], dtype, key_row_start, seq_len, entry_start, B,
                                            T, H, D, max_len, q[l], w[l], bias[l],
                                            l == 0 ? 1 : 2, z_out,
-                                           l == n_idx - 1 ? prob_out : nullptr, stream);
+                                           l == n_idx - 1 ? prob_out : nullptr,
+                                           l == n_idx - 1 ? gate_bits : nullptr, gate_threshold,
+                                           stream);
             if (rc != LSA_OK) return rc;
         }
         return LSA_OK;
@@ -695,6 +745,8 @@ extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dty
     if (B <= 0 || H <= 0 || max_len < 0)
         return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: B=%d H=%d max_len=%lld", B, H,
                     (long long)max_len);
+    if (gate_bits && !aligned16(gate_bits))
+        return fail(LSA_ERR_INVALID_ARG, "lsa_index_score_union: gate_bits must be 16-byte aligned");
     if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "lsa_index_score_union: B=%d > 65535", B);
     if (max_len > (int64_t)1 << 31)
         return fail(LSA_ERR_UNSUPPORTED, "lsa_index_score_union: max_len too large");
@@ -718,7 +770,8 @@ extern "C" int lsa_index_score_union(int n_idx, const void* const* keys, int dty
     hipStream_t st = (hipStream_t)stream;
 #define LSA_UNI(mt, kt)                                                                       \
     hipLaunchKernelGGL((k_score_union<mt, kt>), grid, dim3(256), 0, st, ua, key_row_start,     \
-                       seq_len, entry_start, H, max_len, z_out, prob_out)
+                       seq_len, entry_start, H, max_len, z_out, prob_out, gate_bits,         \
+                       lsa_gate_words(max_len), gate_threshold)
     if (D == 128) {
         if (MT == 1) LSA_UNI(1, 4); else if (MT == 2) LSA_UNI(2, 4); else LSA_UNI(4, 4);
     } else {

@@ -5,11 +5,15 @@
 // entries with I >= 0.5 are fetched, with no fixed count.  I >= 0.5 exactly
 // when the logit z >= 0, so the gate compares the fp32 logit.
 //
-// Two passes over the logits of each sequence, both HBM-streaming:
+// From the logits: two passes over each sequence, both HBM-streaming:
 //   count:   one workgroup per tile of kTile entries writes the tile's count;
 //   scatter: each tile adds the counts of the tiles before it (a few dozen
 //            values, from L2), then writes its kept indices in ascending
 //            order through a workgroup-wide exclusive scan.
+// From gate bits (one 16-bit word per 16 entries, set by the score kernels in
+// the launch that computes the logits): one pass; each tile of kBitTile
+// entries counts the set bits of all earlier tiles itself (1/128 of the
+// logits' bytes), so no count pass runs.
 // The order of the output never depends on scheduling.
 #include <mutex>
 
@@ -143,6 +147,82 @@ __global__ __launch_bounds__(kSelThreads) void k_select_scatter(
     }
 }
 
+constexpr int kBitTile = 8192;                          // entries per workgroup (bit form)
+constexpr int kBitWords = kBitTile / 16;                // gate words per tile (512)
+static_assert(kBitWords == 2 * kSelThreads, "two words per thread");
+
+// Bit form: thread t of tile `tile` owns words 2t, 2t+1 of the tile (32 entries).
+// Every load is issued at once, before the sequence length arrives: the words
+// read are below gstride (a multiple of 8 that covers max_len), so in the
+// caller's rows whatever S is, and bits past S are masked off afterwards.
+__global__ __launch_bounds__(kSelThreads) void k_select_bits(
+    const uint16_t* __restrict__ gate_bits, int64_t gstride,
+    const int64_t* __restrict__ entry_start, const int32_t* __restrict__ seq_len,
+    int64_t max_len, int32_t* __restrict__ cand_idx, int32_t* __restrict__ cand_count) {
+    const int b = blockIdx.y;
+    const int tile = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint16_t* row = gate_bits + (int64_t)b * gstride;   // 16-byte aligned
+    const int len_b = seq_len[b];
+    const int64_t eo = entry_start[b];
+
+    // this thread's two words (w0 even, gstride a multiple of 8: both or neither)
+    const int64_t w0 = (int64_t)tile * kBitWords + 2 * tid;
+    uint32_t bits = w0 < gstride ? *reinterpret_cast<const uint32_t*>(row + w0) : 0u;
+    // the words of the tiles before this one (below tile * kBitWords < gstride)
+    const u32x4* r4 = reinterpret_cast<const u32x4*>(row);
+    const int nq = tile * (kBitWords / 8);                    // 16-byte words before the tile
+    int pre = 0;
+    for (int i0 = tid; i0 < nq; i0 += 4 * kSelThreads) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kSelThreads;
+            v[u] = i < nq ? r4[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            pre += __popc(v[u][0]) + __popc(v[u][1]) + __popc(v[u][2]) + __popc(v[u][3]);
+    }
+    const int64_t S = min((int64_t)len_b, max_len);
+    const int64_t tiles_b = (S + kBitTile - 1) / kBitTile;
+    if (tile > 0 && tile >= tiles_b) return;
+    // earlier tiles are whole (tile < tiles_b), so all their words count; here,
+    // entries past S are masked off (a word holding entry S-1 need not be clean)
+    const int64_t e0 = 16 * w0;
+    const int64_t left = S - e0;
+    if (left < 32) bits &= left > 0 ? (1u << left) - 1u : 0u;
+    const int c = __popc(bits);
+    // one pass of two wave scans: the earlier tiles' total and this tile's
+    // exclusive positions
+    __shared__ int wpre[kSelThreads / kWave];
+    __shared__ int wcnt[kSelThreads / kWave];
+    for (int off = 32; off > 0; off >>= 1) pre += __shfl_xor(pre, off);
+    const int incl = wave_incl_scan(c);
+    const int lane = tid & 63, w = tid >> 6;
+    if (lane == 63) {
+        wpre[w] = pre;
+        wcnt[w] = incl;
+    }
+    lds_barrier();
+    int base = 0, wbefore = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kSelThreads / kWave; ++i) {
+        base += wpre[i];
+        wbefore += i < w ? wcnt[i] : 0;
+        tot += wcnt[i];
+    }
+    int pos = base + wbefore + incl - c;
+    int32_t* out = cand_idx + eo;
+    while (bits) {
+        const int j = __ffs(bits) - 1;
+        out[pos++] = (int32_t)(e0 + j);
+        bits &= bits - 1u;
+    }
+    const bool last_tile = tiles_b == 0 ? (tile == 0) : (tile == tiles_b - 1);
+    if (last_tile && tid == 0) cand_count[b] = base + tot;
+}
+
 }  // namespace lsa
 
 using namespace lsa;
@@ -171,11 +251,17 @@ static int select_launch(const char* who, const float* z, const int64_t* entry_s
     return launch_status(who);
 }
 
+static int select_validate_sizes(const char* who, int B, int64_t max_len);
+
 static int select_validate(const char* who, const float* z, const int64_t* entry_start,
                            const int32_t* seq_len, int B, int64_t max_len,
                            const int32_t* cand_idx, const int32_t* cand_count) {
     if (!z || !entry_start || !seq_len || !cand_idx || !cand_count)
         return fail(LSA_ERR_INVALID_ARG, "%s: a required pointer is NULL", who);
+    return select_validate_sizes(who, B, max_len);
+}
+
+static int select_validate_sizes(const char* who, int B, int64_t max_len) {
     if (B <= 0 || max_len < 0)
         return fail(LSA_ERR_INVALID_ARG, "%s: B=%d max_len=%lld", who, B, (long long)max_len);
     if (B > 65535) return fail(LSA_ERR_UNSUPPORTED, "%s: B=%d > 65535", who, B);
@@ -183,11 +269,28 @@ static int select_validate(const char* who, const float* z, const int64_t* entry
     return LSA_OK;
 }
 
-extern "C" int lsa_select_compact(const float* z, const int64_t* entry_start,
-                                  const int32_t* seq_len, int B, int64_t max_len, float threshold,
-                                  int32_t* cand_idx, int32_t* cand_count, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+extern "C" int lsa_select_compact(const float* z, const uint16_t* gate_bits,
+                                  const int64_t* entry_start, const int32_t* seq_len, int B,
+                                  int64_t max_len, float threshold, int32_t* cand_idx,
+                                  int32_t* cand_count, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
     clear_error();
+    if (gate_bits) {
+        if (!entry_start || !seq_len || !cand_idx || !cand_count)
+            return fail(LSA_ERR_INVALID_ARG, "lsa_select_compact: a required pointer is NULL");
+        if (!aligned16(gate_bits))
+            return fail(LSA_ERR_INVALID_ARG, "lsa_select_compact: gate_bits must be 16-byte aligned");
+        int rc = select_validate_sizes("lsa_select_compact", B, max_len);
+        if (rc != LSA_OK) return rc;
+        rc = check_device(nullptr);
+        if (rc != LSA_OK) return rc;
+        const int64_t t = ceil_div(max_len, kBitTile);
+        dim3 grid((unsigned)(t < 1 ? 1 : t), (unsigned)B);
+        hipLaunchKernelGGL(k_select_bits, grid, dim3(kSelThreads), 0, (hipStream_t)stream,
+                           gate_bits, lsa_gate_words(max_len), entry_start, seq_len, max_len,
+                           cand_idx, cand_count);
+        return launch_status("lsa_select_compact");
+    }
     int rc = select_validate("lsa_select_compact", z, entry_start, seq_len, B, max_len, cand_idx,
                              cand_count);
     if (rc != LSA_OK) return rc;

@@ -1,8 +1,9 @@
 """Device-resident inputs and the four-call decode pipeline over them.
 
 Holds preallocated outputs and workspaces so that one `step()` enqueues
-exactly: index score -> gate/compaction -> top-k -> sparse attention, all in
-liblsa.so kernels on one stream, with no host synchronisation.
+exactly: index score (which also writes the gate bits) -> compaction from the
+bits -> top-k -> sparse attention, all in liblsa.so kernels on one stream,
+with no host synchronisation.
 """
 from __future__ import annotations
 
@@ -81,6 +82,8 @@ class Pipeline:
         self.z = torch.empty(n, dtype=torch.float32, device=dev)
         self.prob = torch.empty(n, dtype=torch.float32, device=dev) if with_prob else None
         self.cand_idx = torch.empty(n, dtype=torch.int32, device=dev)
+        # the gate of z >= 0, one bit per entry, written by the score launch
+        self.gate = torch.empty(B * lsa.lsa_gate_words(d.max_len), dtype=torch.int16, device=dev)
         self.cand_count = torch.empty(B, dtype=torch.int32, device=dev)
         self.ws_select = torch.empty(
             max(1, lsa.lsa_workspace_bytes(lsa.LSA_OP_SELECT, B, max_len=d.max_len)),
@@ -100,7 +103,7 @@ class Pipeline:
         d = self.d
         lsa.lsa_index_score(d.keys[replica % len(d.keys)], d.key_row_start, d.seq_len,
                             d.entry_start, d.max_len, d.q, d.w, d.bias, reduce_max=True,
-                            z_out=self.z, prob_out=self.prob, stream=stream)
+                            z_out=self.z, prob_out=self.prob, gate_bits=self.gate, stream=stream)
 
     def score_union(self, n_indexers: int, replica: int = 0, fused: bool = True, stream=None):
         """OR-mode union of n indexers (key replicas replica .. replica+n-1 stand in
@@ -111,12 +114,15 @@ class Pipeline:
         if fused:
             lsa.lsa_index_score_union(keys, d.key_row_start, d.seq_len, d.entry_start, d.max_len,
                                       [d.q] * n_indexers, [d.w] * n_indexers,
-                                      [d.bias] * n_indexers, self.z, stream=stream)
+                                      [d.bias] * n_indexers, self.z, gate_bits=self.gate,
+                                      stream=stream)
             return
         for i in range(n_indexers):
             lsa.lsa_index_score(keys[i], d.key_row_start, d.seq_len,
                                 d.entry_start, d.max_len, d.q, d.w, d.bias,
-                                reduce_max=1 if i == 0 else 2, z_out=self.z, stream=stream)
+                                reduce_max=1 if i == 0 else 2, z_out=self.z,
+                                gate_bits=self.gate if i == n_indexers - 1 else None,
+                                stream=stream)
 
     def rescore(self, replica: int = 0, stream=None):
         """The native indexer's per-step score of the kept entries, into r."""
@@ -140,6 +146,13 @@ class Pipeline:
                            d.max_len, dst, d.latent_row_start, stream=stream)
 
     def select(self, stream=None):
+        """Compaction from the gate bits the score launch wrote (one launch)."""
+        d = self.d
+        lsa.lsa_select_compact(None, d.entry_start, d.seq_len, d.max_len, self.cand_idx,
+                               self.cand_count, None, gate_bits=self.gate, stream=stream)
+
+    def select_from_logits(self, stream=None):
+        """The same compaction taken on z (a count launch and a scatter launch)."""
         d = self.d
         lsa.lsa_select_compact(self.z, d.entry_start, d.seq_len, d.max_len, self.cand_idx,
                                self.cand_count, self.ws_select, stream=stream)

@@ -19,6 +19,7 @@ MISALIGNED = ctypes.c_void_p(0x10008)
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"static inline[^{]*\{[^}]*\}", "", text)    # header-only helpers
     return sorted(set(re.findall(r"\b(lsa_[a-z_]+)\s*\(", text)))
 
 
@@ -64,27 +65,38 @@ def test_status_strings_and_version(lib):
 def test_index_score_validation(lib):
     P = FAKE
     f = lib.lsa_index_score
-    assert f(None, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1
+    assert f(None, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -1
     assert b"NULL" in lib.lsa_last_error()
-    assert f(P, 1, P, P, P, 0, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1   # B = 0
-    assert f(P, 1, P, P, P, 1, 1, 64, -5, 10, P, P, 0.0, 0, P, None, None) == -1   # D < 0
-    assert f(P, 7, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1  # dtype
-    assert f(MISALIGNED, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -1
+    assert f(P, 1, P, P, P, 0, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -1   # B = 0
+    assert f(P, 1, P, P, P, 1, 1, 64, -5, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -1   # D < 0
+    assert f(P, 7, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -1  # dtype
+    assert f(MISALIGNED, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -1
     assert b"aligned" in lib.lsa_last_error()
     # vector path envelope
-    assert f(P, 0, P, P, P, 1, 64, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -2
-    assert f(P, 1, P, P, P, 70000, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None) == -2
+    assert f(P, 0, P, P, P, 1, 64, 64, 128, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -2
+    assert f(P, 1, P, P, P, 70000, 1, 64, 128, 10, P, P, 0.0, 0, P, None, None, 0.0, None) == -2
+    # gate bits: one logit per entry (T = 1 or a reduction), 16-byte aligned rows
+    assert f(P, 1, P, P, P, 1, 4, 64, 128, 10, P, P, 0.0, 0, P, None, P, 0.0, None) == -1
+    assert b"gate" in lib.lsa_last_error()
+    assert f(P, 1, P, P, P, 1, 1, 64, 128, 10, P, P, 0.0, 0, P, None, MISALIGNED, 0.0, None) == -1
+    assert b"gate_bits" in lib.lsa_last_error()
 
 
 def test_select_validation(lib):
     P = FAKE
     f = lib.lsa_select_compact
-    assert f(None, P, P, 1, 10, 0.0, P, P, P, 1 << 20, None) == -1
-    assert f(P, P, P, 0, 10, 0.0, P, P, P, 1 << 20, None) == -1
+    assert f(None, None, P, P, 1, 10, 0.0, P, P, P, 1 << 20, None) == -1
+    assert f(P, None, P, P, 0, 10, 0.0, P, P, P, 1 << 20, None) == -1
     need = lib.lsa_workspace_bytes(1, 4, 0, 0, 0, 100000, 0, 0)
     assert need >= 4 * 4
-    assert f(P, P, P, 4, 100000, 0.0, P, P, P, need - 1, None) == -3
-    assert f(P, P, P, 4, 100000, 0.0, P, P, None, need, None) == -3
+    assert f(P, None, P, P, 4, 100000, 0.0, P, P, P, need - 1, None) == -3
+    assert f(P, None, P, P, 4, 100000, 0.0, P, P, None, need, None) == -3
+    # the bit form: z and the workspace unused, the rows 16-byte aligned
+    assert f(None, MISALIGNED, P, P, 4, 100000, 0.0, P, P, None, 0, None) == -1
+    assert b"aligned" in lib.lsa_last_error()
+    assert f(None, P, None, P, 4, 100000, 0.0, P, P, None, 0, None) == -1
+    assert f(None, P, P, P, 0, 100000, 0.0, P, P, None, 0, None) == -1
+    assert f(None, P, P, P, 70000, 100000, 0.0, P, P, None, 0, None) == -2
 
 
 def test_select_noalloc_validation(lib):
@@ -187,7 +199,7 @@ def test_workspace_sizes(lib):
 def test_score_reduce_mode_validation(lib):
     P = FAKE
     f = lib.lsa_index_score
-    base = [P, 1, P, P, P, 2, 1, 64, 128, 1000, P, P, 0.0, 1, P, None, None]
+    base = [P, 1, P, P, P, 2, 1, 64, 128, 1000, P, P, 0.0, 1, P, None, None, 0.0, None]
     for mode in (-1, 3):
         a = list(base); a[13] = mode
         assert f(*a) == -1
@@ -221,7 +233,7 @@ def test_score_union_validation(lib):
     arr = ctypes.c_void_p * 4
     ks, qs, ws = arr(P, P, P, P), arr(P, P, P, P), arr(P, P, P, P)
     bs = (ctypes.c_float * 4)(0.0, 0.0, 0.0, 0.0)
-    base = [3, ks, 1, P, P, P, 2, 1, 64, 128, 1000, qs, ws, bs, P, None, None]
+    base = [3, ks, 1, P, P, P, 2, 1, 64, 128, 1000, qs, ws, bs, P, None, None, 0.0, None]
     for i in (1, 11, 12, 13):                       # the host arrays
         a = list(base); a[i] = None
         assert f(*a) == -1, i
@@ -238,6 +250,9 @@ def test_score_union_validation(lib):
     assert f(*a) == -1
     a = list(base); a[6] = 70000                    # B too large
     assert f(*a) == -2
+    a = list(base); a[16] = MISALIGNED              # gate bits
+    assert f(*a) == -1
+    assert b"gate_bits" in lib.lsa_last_error()
     # shapes outside the fused launch go through lsa_index_score's own checks
     a = list(base); a[2] = 7                        # dtype
     assert f(*a) == -1
