@@ -17,8 +17,10 @@
 // Few tokens (decode: one per sequence) make each product a stream of the
 // weights, bound by HBM: k_encode_skinny gives every workgroup 16 weight rows
 // and splits K over its waves, each wave holding all the tokens' rows in
-// registers, so every weight byte is read once.  Many tokens (a burst of tau
-// positions): k_encode_tiled, an LDS-tiled product bound by the matrix cores.
+// registers, so every weight byte is read once; for up to 8 tokens and a long
+// K, k_encode_rows gives a workgroup 4 rows (vector dot products) so that
+// more workgroups stream at once.  Many tokens (a burst of tau positions):
+// k_encode_tiled, an LDS-tiled product bound by the matrix cores.
 #include "common.hpp"
 
 // LDS stages of the tiled product per tile shape
@@ -127,6 +129,89 @@ __global__ __launch_bounds__(WAVES * kWave) void k_encode_skinny(EncGemm g) {
         for (int w = 0; w < WAVES; ++w) sum += red[w][t][v][l];
         const int m = 16 * t + 4 * (l >> 4) + v, n = n0 + (l & 15);
         if (m < g.M && n < g.N) enc_store(g, m, n, sum);
+    }
+}
+
+// ---------------------------------------------------------- fewest tokens
+// M <= 8 (decode: one token per sequence): a plain vector product, as the
+// matrix cores would idle on 8 token rows.  Workgroup = R weight rows, so the
+// down product's 1600 rows give 400 workgroups and every CU streams weights
+// (16-row blocks gave 100).  Thread t takes the 8-element K chunks t, t + 256,
+// ... of all R rows and all MT token rows (U chunks in flight) and keeps R x MT
+// fp32 sums, accumulated with bf16 pair dot products (the products of two bf16
+// values are exact in fp32); the 256 threads' sums meet through LDS in a fixed
+// order (deterministic): 8 slices of 32 threads each, then the 8 slice sums.
+// Token rows past M are computed on row M-1 and never stored; weight rows past
+// N likewise.
+template <int R, int MT, int U>
+__global__ __launch_bounds__(256) void k_encode_rows(EncGemm g) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    constexpr int NV = R * MT;                   // sums per thread
+    constexpr int SL = 256 / NV;                 // slices of the first reduction step
+    static_assert(NV * SL == 256 && NV <= 64, "reduction layout");
+    // row stride NV + 1: the 64 lanes of a read fall on 64 distinct banks
+    __shared__ float part[256][NV + 1];
+    __shared__ float slice[SL][NV];
+    const int tid = threadIdx.x;
+    const int n0 = blockIdx.x * R;
+    const bf16* brow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) brow[r] = enc_brow(g, min(n0 + r, g.N - 1));
+    const bf16* arow[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) arow[m] = g.a + (int64_t)min(m, g.M - 1) * g.lda;
+    const int nch = g.K / 8;
+    float acc[R][MT];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+    for (int c0 = tid; c0 < nch; c0 += 256 * U) {
+        bf16x8 bw[U][R], av[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = min(c0 + 256 * u, nch - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) bw[u][r] = load8(brow[r] + 8 * c);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) av[u][m] = load8(arow[m] + 8 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (c0 + 256 * u < nch) {
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const bf16x2 x = {bw[u][r][2 * j], bw[u][r][2 * j + 1]};
+                            const bf16x2 y = {av[u][m][2 * j], av[u][m][2 * j + 1]};
+                            acc[r][m] = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc[r][m], false);
+                        }
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) part[tid][r * MT + m] = acc[r][m];
+    __syncthreads();
+    {
+        // thread t adds sum v = t % NV of the NV threads of slice t / NV, in order
+        const int v = tid % NV, sl = tid / NV;
+        float x = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < NV; ++j) x += part[NV * sl + j][v];
+        slice[sl][v] = x;
+    }
+    __syncthreads();
+    if (tid < NV) {
+        float x = 0.0f;
+#pragma unroll
+        for (int sl = 0; sl < SL; ++sl) x += slice[sl][tid];
+        const int r = tid / MT, m = tid % MT;
+        if (m < g.M && n0 + r < g.N) enc_store(g, m, n0 + r, x);
     }
 }
 
@@ -284,7 +369,20 @@ __global__ __launch_bounds__(256) void k_encode_tiled(EncGemm g, int tiles_m, in
 
 constexpr int kEncSkinnyMaxM = 32;   // token rows the few-token kernel keeps in registers
 
+constexpr int kEncRowsMaxM = 8;      // token rows the vector kernel takes
+constexpr int kEncRows = 4;          // weight rows per workgroup of the vector kernel
+constexpr int kEncRowsMinK = 4096;   // depth from which it beats the 16-row kernel
+
 static int launch_product(const EncGemm& g, int num_cus, hipStream_t st) {
+    // Up to 8 tokens and a long K (the down product, 7168 deep): 4-row
+    // workgroups, 21.8 -> 17.0 us per 8-token call at 7168 -> 1536 -> 64 x 128
+    // in one A/B (the up product, 1536 deep, stays on the 16-row kernel: its
+    // 8192 rows already give 512 workgroups).
+    if (g.M <= kEncRowsMaxM && g.K >= kEncRowsMinK) {
+        const dim3 grid((unsigned)ceil_div(g.N, kEncRows));
+        hipLaunchKernelGGL((k_encode_rows<kEncRows, kEncRowsMaxM, 1>), grid, dim3(256), 0, st, g);
+        return launch_status("query_encode");
+    }
     if (g.M <= kEncSkinnyMaxM) {
         const dim3 grid((unsigned)ceil_div(g.N, 16));
         // long K: 16 waves share it, so more weight loads are in flight per row block

@@ -90,6 +90,8 @@ def _sample_rows(M, n=24, seed=0):
     (5, 512, 128, 4, 32),       # few tokens: weight-streaming kernel, one 16-row tile
     (17, 256, 192, 3, 40),      # two token tiles, ragged N (H*D = 120), gate past a tile edge
     (32, 4096, 64, 2, 64),      # long K: 16 waves share it
+    (3, 4096, 192, 3, 40),      # few tokens, long K: 4-row vector kernel, ragged last block
+    (8, 8192, 64, 1, 64),       # eight tokens, long K, the gate row alone in the last block
     (33, 192, 64, 3, 40),       # many tokens, small tiles, ragged everywhere
     (300, 512, 256, 8, 64),     # small tiles, ragged M
     (520, 256, 512, 64, 128),   # up product on large tiles (enough to fill the chip), ragged M
