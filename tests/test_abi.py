@@ -39,6 +39,23 @@ def test_header_declares_the_calls():
     assert sorted(binding.EXPORTED) == syms
 
 
+def test_header_compiles_as_c99_and_cpp17(tmp_path):
+    """The boundary header is plain C: it builds warning-free as C99 and as C++17,
+    and its header-only helper gives the documented gate row length."""
+    src = tmp_path / "use.c"
+    src.write_text('#include "lsa.h"\n'
+                   "int main(void) {\n"
+                   "    return lsa_gate_words(0) == 0 && lsa_gate_words(1) == 8 &&\n"
+                   "           lsa_gate_words(128) == 8 && lsa_gate_words(129) == 16 ? 0 : 1;\n"
+                   "}\n")
+    inc = os.path.dirname(HEADER)
+    for cmd in (["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror"],
+                ["g++", "-std=c++17", "-Wall", "-Wextra", "-pedantic", "-Werror", "-x", "c++"]):
+        exe = tmp_path / ("use_" + cmd[0].replace("+", "p"))
+        subprocess.run(cmd + ["-I", inc, str(src), "-o", str(exe)], check=True)
+        assert subprocess.run([str(exe)]).returncode == 0
+
+
 def test_every_declared_symbol_is_exported(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
