@@ -164,7 +164,7 @@ def timed_eager(torch, stream, calls, launches, intervals=5, warm=1):
     return statistics.median(res)
 
 
-def timed_graph(torch, stream, g, launches, intervals=7, warm=2):
+def timed_graph(torch, stream, g, launches, intervals=10, warm=3):
     """Median seconds per launch over `intervals` replays of graph `g`, which holds
     `launches` launches; HIP events recorded on `stream`, where the graph runs."""
     res = []
@@ -440,11 +440,11 @@ def main():
 
         # per-kernel launch durations: graphs of R back-to-back launches of one call
         def reps_for(est_s):
-            return args.kernel_reps or max(8, min(200, int(2e-3 / max(est_s, 1e-6)) + 1))
+            return args.kernel_reps or max(8, min(400, int(2e-3 / max(est_s, 1e-6)) + 1))
         r = reps_for(step_s / 2)
         t_score = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.score(i) for i in range(r)]), r)
-        r = reps_for(1e-5)
+        r = reps_for(4e-6)
         t_select = timed_graph(torch, stream, capture(torch, stream, [p.select] * r), r)
         t_select_z = timed_graph(torch, stream, capture(torch, stream, [p.select_from_logits] * r),
                                  r)
@@ -453,6 +453,10 @@ def main():
         t_floor = timed_graph(torch, stream, capture(torch, stream, [lambda: floor_e.add_(1)] * r),
                               r)
         t_topk = timed_graph(torch, stream, capture(torch, stream, [p.topk] * r), r)
+        # a1 + a2 as the step runs them: the score with its gate bits, then the compaction
+        rs = reps_for(step_s / 2)
+        t_score_gate = timed_graph(torch, stream, capture(
+            torch, stream, [f for i in range(rs) for f in (lambda i=i: p.score(i), p.select)]), rs)
         r = reps_for(step_s / 4)
         t_attend = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.attend(i) for i in range(r)]), r)
@@ -588,6 +592,7 @@ def main():
                    "hca_rows_per_seq": wl.max_hca, "parallelism": "single GPU"},
         "kernels_us": {"index_score": round(t_score * 1e6, 2),
                        "select_compact": round(t_select * 1e6, 2),
+                       "index_score_and_gate": round(t_score_gate * 1e6, 2),
                        "select_compact_from_logits": round(t_select_z * 1e6, 2),
                        "one_element_add_floor": round(t_floor * 1e6, 2),
                        "topk": round(t_topk * 1e6, 2),
