@@ -248,10 +248,13 @@ def cpu_burst_prefix(wl, prefix_all: int = 2048, prefix_one: int = 256):
                       f"threads ({dt:.2f} s), the first {prefix_one} on one ({dt1:.2f} s)"}
 
 
-def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, nbytes: int = 1 << 30):
+def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, read_bytes: int,
+                 nbytes: int = 1 << 30):
     """Ceilings measured in this run by libceiling.so (the best over a few grid sizes):
-    a 1 GiB streaming read, a 1 GiB copy (read + write bytes counted), and a gather
-    of `gather_rows` random rows of `row_bytes` (the attention launch's row count and
+    a 1 GiB streaming read, a 1 GiB copy (read + write bytes counted), a streaming
+    read of `read_bytes` (the score launch's size, so its launch ramp and tail
+    weigh as they do in the score; four buffers rotate), and a gather of
+    `gather_rows` random rows of `row_bytes` (the attention launch's row count and
     row size) from a 4 GiB pool, rotating over 24 index lists; GB/s."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(REPO, "lookahead_sparse_kv_amd", "libceiling.so"))
@@ -275,6 +278,12 @@ def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, nbytes: int = 
     t_copy = best(lambda g: ok(lib.ceiling_copy(a.data_ptr(), b.data_ptr(), nbytes, g, st)), 4,
                   (1024, 2048, 4096, 8192))
     del a, b
+    rb = read_bytes // 16 * 16
+    bufs = [torch.ones(rb // 4, dtype=torch.int32, device="cuda") for _ in range(4)]
+    t_read_same = min(timed_graph(torch, stream, capture(torch, stream, [
+        lambda i=i, g=g: ok(lib.ceiling_read(bufs[i % 4].data_ptr(), rb, g, sink.data_ptr(), st))
+        for i in range(8)]), 8) for g in (1024, 2048, 4096, 8192))
+    del bufs
     pool_rows = (4 << 30) // row_bytes
     pool = torch.empty(pool_rows * row_bytes // 4, dtype=torch.int32, device="cuda").fill_(5)
     gen = torch.Generator(device="cuda").manual_seed(1)
@@ -287,6 +296,7 @@ def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, nbytes: int = 
     del pool, lists
     return {"read_GBs": round(nbytes / t_read / 1e9, 1),
             "copy_GBs": round(2 * nbytes / t_copy / 1e9, 1),
+            "read_GBs_score_size": round(rb / t_read_same / 1e9, 1), "score_size_bytes": rb,
             "gather_GBs": round(gather_rows * row_bytes / t_gather / 1e9, 1),
             "gather": f"{gather_rows} random {row_bytes}-byte rows (sorted indices) per launch",
             "bytes": nbytes}
@@ -524,7 +534,8 @@ def main():
                    "topk": single_launch_us(torch, stream, p.topk),
                    "sparse_attend": single_launch_us(torch, stream, p.attend),
                    "step": single_launch_us(torch, stream, p.step)}
-        hbm = measured_hbm(torch, stream, att_rows, wl.Dl * wl.latent.itemsize)
+        hbm = measured_hbm(torch, stream, att_rows, wl.Dl * wl.latent.itemsize,
+                           int(wl.seq_len.sum()) * wl.D * 2 if wl.T == 1 else 1 << 28)
     burst = None
     if wl.T == 1:
         # the tau-burst trigger score on its own workload, beside the decode step
@@ -564,6 +575,9 @@ def main():
     if wl.T == 1:
         roofline = roof("hbm", score_bytes, t_score, HBM_PEAK_GBS, "GB/s",
                         read_traffic("score_decode", args.workload, "score.hip"))
+        # against a plain streaming read of the same size in one launch
+        roofline["frac_of_measured_read_same_size"] = round(
+            roofline["achieved"] / hbm["read_GBs_score_size"], 4)
     else:
         roofline = roof("mfma", score_flops, t_score, BF16_PEAK_TFLOPS, "TFLOP/s", None)
     ta, tc = (read_traffic("attend", args.workload, "attend.hip"),
