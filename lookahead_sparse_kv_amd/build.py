@@ -61,6 +61,25 @@ def _link(objs, lib: str) -> None:
     os.replace(tmp, lib)
 
 
+REPO = os.path.dirname(HERE)
+C_HOST_SRC = os.path.join(REPO, "tests", "c_host", "decode_step.cpp")
+C_HOST_BIN = os.path.join(REPO, "tests", "c_host", "decode_step")
+
+
+def _build_c_host() -> None:
+    """The tests' plain C++ caller of the C ABI (host code only, linked to liblsa.so)."""
+    if not os.path.exists(C_HOST_SRC):
+        return
+    tmp = C_HOST_BIN + ".tmp"
+    cmd = [HIPCC, "-std=c++17", "-O2", f"--offload-arch={ARCH}", "-I",
+           os.path.join(REPO, "include"), C_HOST_SRC, "-L", HERE, "-llsa",
+           "-Wl,-rpath,$ORIGIN/../../lookahead_sparse_kv_amd", "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, C_HOST_BIN)
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + ["ceiling.hip"]
@@ -68,8 +87,9 @@ def build(verbose: bool = True) -> str:
         objs = list(ex.map(_compile, srcs))
     _link(objs[:-1], LIB)
     _link(objs[-1:], CEILING_LIB)
+    _build_c_host()
     if verbose:
-        print(f"built {LIB} and {CEILING_LIB}")
+        print(f"built {LIB}, {CEILING_LIB} and {C_HOST_BIN}")
     return LIB
 
 

@@ -288,3 +288,13 @@ def test_union_binding_checks_its_lists():
         binding.lsa_index_score_union([k, k], i64, i32, i64, 4, [q], [w, w], [0.0, 0.0], z)
     with pytest.raises(ValueError):
         binding.lsa_index_score_union([k], i64, i32, i64, 4, [q], [w], [0.0, 1.0], z)
+
+
+def test_c_host_program_is_built():
+    """The plain C++ caller used by the GPU tests links against liblsa.so and runs
+    (given no arguments it prints its usage before touching the GPU)."""
+    from lookahead_sparse_kv_amd import build
+    if not os.path.exists(build.C_HOST_BIN):
+        pytest.fail("tests/c_host/decode_step is not built; run python -m lookahead_sparse_kv_amd.build")
+    r = subprocess.run([build.C_HOST_BIN], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
