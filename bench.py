@@ -389,10 +389,9 @@ def main():
     wl = inputs.make_workload(args.workload)
     key_bytes = wl.keys.nbytes
     rk = max(1, -(-ROTATE_BYTES // key_bytes))
-    # bytes the attention touches per launch (top-k rows + HCA rows)
-    att_rows = wl.B * (wl.k + wl.max_hca)
-    att_bytes = att_rows * wl.Dl * 2
-    rl = max(1, -(-ROTATE_BYTES // att_bytes))
+    # an upper bound of the bytes the attention touches per launch (k top-k rows
+    # and max_hca HCA rows per sequence): sizes the replica rotation
+    rl = max(1, -(-ROTATE_BYTES // (wl.B * (wl.k + wl.max_hca) * wl.Dl * 2)))
     if args.profile_launches:
         # three key sets so the union's indexers read distinct keys, as in the timed runs
         rk, rl = (3 if wl.T == 1 else 1), 1
@@ -434,6 +433,11 @@ def main():
         nrot = max(rk, rl)
         p.step(0)
         torch.cuda.synchronize()
+        # the rows each attention launch attends: the step's top-k rows plus every
+        # HCA row of each sequence (ragged workloads attend fewer than k + max_hca)
+        att_topk = int(np.minimum(p.topk_count.cpu().numpy(), wl.k).sum())
+        att_hca = int(np.minimum(wl.hca_count, wl.max_hca).sum()) if wl.hca is not None else 0
+        att_rows = att_topk + att_hca
         if args.warmup:
             capture(torch, stream, [lambda i=i: p.step(i) for i in range(args.warmup)]).replay()
         timed = capture(torch, stream,
@@ -553,8 +557,9 @@ def main():
     score_flops = 2.0 * scores_per_step * wl.H * wl.D
     # union of three indexers in one launch: three key sets, queries and gates, one logit write
     union3_bytes = 3 * (score_bytes - int(wl.seq_len.sum()) * 4) + int(wl.seq_len.sum()) * 4
-    att_alg_bytes = att_bytes + wl.qa.nbytes * 2 + wl.B * wl.k * 4   # rows, qa in, out, indices
-    att_flops = 4.0 * wl.B * wl.T * wl.Hq * (wl.k + wl.max_hca) * wl.Dl
+    # attended rows, qa in, out, top-k indices
+    att_alg_bytes = att_rows * wl.Dl * 2 + wl.qa.nbytes * 2 + att_topk * 4
+    att_flops = 4.0 * wl.T * wl.Hq * att_rows * wl.Dl
     # native re-score: per candidate one key row, its index and its logit; the queries
     rescore_bytes = int(counts.sum()) * (wl.D * 2 + 4 + 4) + wl.B * wl.H * (wl.D * 2 + 4)
 
@@ -622,6 +627,7 @@ def main():
         "decode_tokens_per_s_native_topk": round(
             wl.B * wl.T / (t_attend + t_rescore + t_topk_native + (t_score + t_select) / 64.0), 1),
         "selected_fraction": round(float(counts.sum()) / float(wl.seq_len.sum()), 4),
+        "attended_rows_per_step": att_rows,
         "roofline": roofline,
         "roofline_attend": roof_att,
         "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s",
