@@ -196,22 +196,25 @@ def _topk_gpu(r, lens, es, cand, cnt, k, max_len):
     ([9000, 300], 7, "signed_zero_nan"),
     ([40000, 100000], 2048, "ties"),          # > LDS capacity: global-key path
     ([70000], 65536, "normal"),
+    ([32768, 32769], 2048, "ties_all"),       # every entry kept: the register path's
+    ([32768, 32769], 30000, "normal_all"),    # capacity exactly, and one past it
 ])
 def test_topk_bit_exact(ref, lens, k, kind):
     rng = np.random.default_rng(len(lens) * 1000 + k)
     lens = np.array(lens, np.int32)
     es = np.concatenate([[0], np.cumsum(lens[:-1])]).astype(np.int64)
     n = int(lens.sum())
-    if kind == "ties":
+    if kind.startswith("ties"):
         r = rng.integers(-3, 40, size=n).astype(np.float32)
-    elif kind == "normal":
+    elif kind.startswith("normal"):
         r = rng.standard_normal(n).astype(np.float32) + 1.0
     else:
         r = rng.integers(-1, 3, size=n).astype(np.float32)
         r[r == 0] = np.where(rng.random((r == 0).sum()) < 0.5, -0.0, 0.0)
         r[rng.choice(n, size=n // 10, replace=False)] = np.nan
-    # candidates: a random half of the entries (ascending), from the reference's gate
-    gate = np.where(rng.random(n) < 0.6, 1.0, -1.0)
+    # candidates: a random 60 % of the entries (all of them for kinds *_all), in
+    # ascending order, from the reference's gate
+    gate = np.where(rng.random(n) < (1.0 if kind.endswith("_all") else 0.6), 1.0, -1.0)
     cand, cnt = ref.select(gate, es, lens)
     announce(f"topk lens={lens.tolist()} k={k} kind={kind}")
     ti, tc = _topk_gpu(r, lens, es, cand, cnt, k, int(lens.max()))
@@ -291,6 +294,20 @@ def test_attend_bf16(ref, B, T, Hq, Dl, lens, counts, hca, k):
     announce(f"attend B={B} T={T} Hq={Hq} Dl={Dl} counts={counts} hca={hca}")
     o, l = _attend_gpu(wl, idx, cnt)
     orf, lr = _attend_ref(ref, wl, idx, cnt)
+    check_attention(o, orf, l, lr)
+
+
+def test_attend_many_splits(ref):
+    """One sequence with 2048 top-k rows and 200 000 HCA rows: about 250 row
+    splits, so the merge of the splits runs over several batches of them."""
+    wl = inputs.random_small(4242, 1, 1, 4, 32, [3000], k=2048, Hq=64, Dl=512,
+                             hca_lens=[200000])
+    rng = np.random.default_rng(42)
+    idx, cnt = _random_indices(rng, wl.seq_len, wl.k, [2048])
+    announce("attend 2048 + 200000 rows, ~250 row splits")
+    o, l = _attend_gpu(wl, idx, cnt)
+    with ref.threads():
+        orf, lr = _attend_ref(ref, wl, idx, cnt)
     check_attention(o, orf, l, lr)
 
 
