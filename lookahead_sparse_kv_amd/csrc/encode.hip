@@ -19,7 +19,8 @@
 // and splits K over its waves, each wave holding all the tokens' rows in
 // registers, so every weight byte is read once; for up to 8 tokens and a long
 // K, k_encode_rows gives a workgroup 4 rows (vector dot products) so that
-// more workgroups stream at once.  Many tokens (a burst of tau positions):
+// more workgroups stream at once; one token, k_encode_stream, an equal share of
+// the rows per CU with every load in flight.  Many tokens (a burst of tau positions):
 // k_encode_tiled, an LDS-tiled product bound by the matrix cores.
 #include "common.hpp"
 
@@ -215,6 +216,116 @@ __global__ __launch_bounds__(256) void k_encode_rows(EncGemm g) {
     }
 }
 
+// The 64 lanes' sums of v[0 .. NV-1] (NV a power of two, at most 64): exchanges
+// that halve the values a lane carries over lane distances 32, 16, .., 64/NV,
+// then plain exchanges over the distances left.  Lane l ends with the sum of
+// value l / (64 / NV) over all 64 lanes, added in an order fixed by the lane
+// pattern alone.
+// 16 bytes at byte offset off of a buffer (zeros past its range).
+__device__ __forceinline__ bf16x8 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int HALF, int OFF>
+__device__ __forceinline__ void wave_halve(float* v, int lane) {
+    const bool up = (lane & OFF) != 0;
+#pragma unroll
+    for (int i = 0; i < HALF; ++i) {
+        const float keep = up ? v[i + HALF] : v[i];
+        const float send = up ? v[i] : v[i + HALF];
+        v[i] = keep + __shfl_xor(send, OFF);
+    }
+    if constexpr (HALF > 1) wave_halve<HALF / 2, OFF / 2>(v, lane);
+}
+
+template <int NV>
+__device__ __forceinline__ float wave_sum_each(float (&v)[NV], int lane) {
+    if constexpr (NV > 1) wave_halve<NV / 2, 32>(v, lane);
+    float x = v[0];
+#pragma unroll
+    for (int off = 32 / NV; off >= 1; off /= 2) x += __shfl_xor(x, off);
+    return x;
+}
+
+// ------------------------------------------------------ few tokens, streamed
+// Up to MT token rows against weight rows that stream through the registers,
+// each weight byte read once.  Workgroup i of G takes rows N i / G .. N (i+1) /
+// G - 1, so every CU streams the same number of rows (the grid holds at least
+// one workgroup per CU).  Its waves form NG row groups of WPG waves; group g
+// takes the workgroup's rows g, g + NG, .. (RPT at most), and its threads the
+// 8-element K chunks t, t + 64 WPG, .. (CPT at most).  A thread loads its
+// chunks of the MT token rows once, then its chunks of every row (all RPT x
+// CPT loads in flight), and accumulates RPT x MT fp32 sums with bf16 pair dot
+// products (bf16 products are exact in fp32).  The sums meet across the
+// group's lanes by wave_sum_each, then across its waves through LDS in wave
+// order, so the result does not depend on scheduling.  Token rows past M and
+// rows past the workgroup's range are computed on a clamped row and never
+// stored.
+template <int MT, int NG, int WPG, int CPT, int RPT>
+__global__ __launch_bounds__(NG * WPG * kWave) void k_encode_stream(EncGemm g) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    constexpr int TG = WPG * kWave;              // threads of a row group
+    constexpr int NV = RPT * MT;                 // sums per thread
+    constexpr int LPV = kWave / NV;              // lanes that end with the same sum
+    static_assert((NV & (NV - 1)) == 0 && NV <= kWave, "butterfly layout");
+    __shared__ float red[NG][WPG][kWave];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / WPG, wv = wave - grp * WPG;
+    const int t = wv * kWave + lane;
+    const int r0 = (int)((int64_t)g.N * blockIdx.x / gridDim.x);
+    const int r1 = (int)((int64_t)g.N * (blockIdx.x + 1) / gridDim.x);
+    // Buffer loads with the row's byte range: chunks past the row's end read
+    // zeros, so the products below need no branch (a branch would let the
+    // compiler sink the first weight load behind the others and wait for all).
+    const int range = g.K * 2;
+    bf16x8 av[CPT][MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(g.a + (int64_t)min(m, g.M - 1) * g.lda), (short)0, range, kBufferWord3);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) av[j][m] = buffer_load8(ar, 16 * (t + TG * j));
+    }
+    bf16x8 bw[RPT][CPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)enc_brow(g, min(r0 + grp + NG * r, r1 - 1)), (short)0, range, kBufferWord3);
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) bw[r][j] = buffer_load8(br, 16 * (t + TG * j));
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first product
+    float acc[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const bf16x2 x = {bw[r][j][2 * p], bw[r][j][2 * p + 1]};
+                    const bf16x2 y = {av[j][m][2 * p], av[j][m][2 * p + 1]};
+                    acc[r * MT + m] = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc[r * MT + m], false);
+                }
+    float s = wave_sum_each<NV>(acc, lane);
+    if constexpr (WPG > 1) {
+        red[grp][wv][lane] = s;
+        __syncthreads();
+        if (wv != 0) return;
+#pragma unroll
+        for (int w = 1; w < WPG; ++w) s += red[grp][w][lane];
+    }
+    if (lane % LPV == 0) {
+        const int i = lane / LPV, r = i / MT, m = i - r * MT;
+        const int n = r0 + grp + NG * r;
+        if (m < g.M && n < r1) enc_store(g, m, n, s);
+    }
+}
+
 // ------------------------------------------------------------ many tokens
 // Workgroup tile (64 WM) x (64 WN), four waves in a 2 x 2 grid, each owning a
 // (32 WM) x (32 WN) block of 32x32x16 matrix-core tiles.  K advances BK at a
@@ -369,11 +480,50 @@ __global__ __launch_bounds__(256) void k_encode_tiled(EncGemm g, int tiles_m, in
 
 constexpr int kEncSkinnyMaxM = 32;   // token rows the few-token kernel keeps in registers
 
+#ifndef LSA_ENC_STREAM
+#define LSA_ENC_STREAM 1
+#endif
+
+// One token row (batch-1 decode), if K is in the streamed kernel's range: up
+// to 256 chunks per row on single-wave row groups of 4 rows (8 groups per
+// workgroup), up to 1024 chunks on one 8-wave group of 8 rows; one workgroup
+// per CU, or more when the rows would not fit.  15.1 -> 13.4 us per call at
+// 7168 -> 1536 -> 64 x 128 in one A/B.  With 4 or 8 token rows the products
+// (4 x 4 dot products per chunk per row) finish after the last rows land and
+// the call was slower (15.8 -> 17.8 and 17.4 -> 18.0 us), as was a matrix-core
+// form with the token rows staged in LDS (17.5 us at 8 rows, 14.6 at one):
+// every workgroup then reads the whole token block, 29 MB over the chip at 8
+// rows against 23 MB of weights.
+static bool launch_stream(const EncGemm& g, int num_cus, hipStream_t st) {
+    const int nch = g.K / 8;
+    if (nch <= 4 * kWave) {
+        constexpr int NG = 8, RPT = 4;
+        const dim3 grid((unsigned)std::min<int64_t>(
+            g.N, std::max<int64_t>(num_cus, ceil_div(g.N, NG * RPT))));
+        const dim3 block(NG * kWave);
+        switch ((nch + kWave - 1) / kWave) {
+            case 1: hipLaunchKernelGGL((k_encode_stream<1, NG, 1, 1, RPT>), grid, block, 0, st, g); break;
+            case 2: hipLaunchKernelGGL((k_encode_stream<1, NG, 1, 2, RPT>), grid, block, 0, st, g); break;
+            case 3: hipLaunchKernelGGL((k_encode_stream<1, NG, 1, 3, RPT>), grid, block, 0, st, g); break;
+            default: hipLaunchKernelGGL((k_encode_stream<1, NG, 1, 4, RPT>), grid, block, 0, st, g); break;
+        }
+        return true;
+    }
+    if (nch <= 2 * 8 * kWave) {
+        constexpr int WPG = 8, RPT = 8;
+        const dim3 grid((unsigned)std::min<int64_t>(g.N, std::max<int64_t>(num_cus, ceil_div(g.N, RPT))));
+        hipLaunchKernelGGL((k_encode_stream<1, 1, WPG, 2, RPT>), grid, dim3(WPG * kWave), 0, st, g);
+        return true;
+    }
+    return false;
+}
+
 constexpr int kEncRowsMaxM = 8;      // token rows the vector kernel takes
 constexpr int kEncRows = 4;          // weight rows per workgroup of the vector kernel
 constexpr int kEncRowsMinK = 4096;   // depth from which it beats the 16-row kernel
 
 static int launch_product(const EncGemm& g, int num_cus, hipStream_t st) {
+    if (LSA_ENC_STREAM && g.M == 1 && launch_stream(g, num_cus, st)) return launch_status("query_encode");
     // Up to 8 tokens and a long K (the down product, 7168 deep): 4-row
     // workgroups, 21.8 -> 17.0 us per 8-token call at 7168 -> 1536 -> 64 x 128
     // in one A/B (the up product, 1536 deep, stays on the 16-row kernel: its

@@ -87,6 +87,8 @@ def _sample_rows(M, n=24, seed=0):
 
 @pytest.mark.parametrize("M,d_model,rank,H,D", [
     (1, 256, 64, 2, 32),        # one token
+    (1, 4096, 192, 3, 40),      # one token: K split over 8 waves, one row per workgroup (195)
+    (1, 4608, 2560, 2, 64),     # one token: more row blocks than CUs (2562 rows, 8 per block)
     (5, 512, 128, 4, 32),       # few tokens: weight-streaming kernel, one 16-row tile
     (17, 256, 192, 3, 40),      # two token tiles, ragged N (H*D = 120), gate past a tile edge
     (32, 4096, 64, 2, 64),      # long K: 16 waves share it
@@ -105,10 +107,10 @@ def test_encode_parity(ref, M, d_model, rank, H, D):
     _check(rows, h, wd, wu, wg, H, D, got, ref.query_encode(h[rows], wd, wu, wg, H, D))
 
 
-@pytest.mark.parametrize("M", [8, 1024])
+@pytest.mark.parametrize("M", [1, 8, 1024])
 def test_encode_full_size_sampled(ref, M):
     """The benchmark's sizes (d_model 7168, rank 1536, 64 heads of 128): decode
-    (8 tokens) and the tau-burst (1024 tokens), reference on sampled tokens."""
+    (1 and 8 tokens) and the tau-burst (1024 tokens), reference on sampled tokens."""
     H, D = 64, 128
     wd, wu, wg = inputs.encoder_weights(H, D)
     h = inputs.hidden_states(M)
@@ -119,6 +121,7 @@ def test_encode_full_size_sampled(ref, M):
 
 
 @pytest.mark.parametrize("M,d_model,rank,H,D", [
+    (1, 7168, 1536, 64, 128),
     (8, 7168, 1536, 64, 128),
     (200, 1024, 256, 16, 64),
 ])
