@@ -302,6 +302,28 @@ def measured_hbm(torch, stream, gather_rows: int, row_bytes: int, read_bytes: in
             "bytes": nbytes}
 
 
+def measured_row_gather(torch, stream, pools, rows, row_bytes: int):
+    """A plain gather (libceiling.so) of the given pool rows, in the given order,
+    rotating over `pools` (replicas of one pool, as the kernel it rates reads
+    them); the best over a few grid sizes; GB/s."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(REPO, "lookahead_sparse_kv_amd", "libceiling.so"))
+    P, L, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ceiling_gather.argtypes = [P, P, L, L, I, P, P]
+    st = ctypes.c_void_p(stream.cuda_stream)
+    idx = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int32)).cuda()
+    sink = torch.zeros(8192, dtype=torch.int32, device="cuda")
+    n = len(pools)
+
+    def ok(rc):
+        assert rc == 0, f"ceiling kernel launch failed ({rc})"
+    t = min(timed_graph(torch, stream, capture(torch, stream, [
+        lambda i=i, g=g: ok(lib.ceiling_gather(pools[i % n].data_ptr(), idx.data_ptr(), len(rows),
+                                               row_bytes, g, sink.data_ptr(), st))
+        for i in range(max(n, 8))]), max(n, 8)) for g in (256, 512, 1024, 2048))
+    return len(rows) * row_bytes / t / 1e9
+
+
 def measured_mfma(torch, stream, n: int = 8192, reps: int = 8):
     """The bf16 matrix rate a library GEMM reaches in this run, as a measured
     ceiling for matrix-core-bound kernels: torch.mm (hipBLASLt) of two n x n bf16
@@ -540,6 +562,16 @@ def main():
                    "step": single_launch_us(torch, stream, p.step)}
         hbm = measured_hbm(torch, stream, att_rows, wl.Dl * wl.latent.itemsize,
                            int(wl.seq_len.sum()) * wl.D * 2 if wl.T == 1 else 1 << 28)
+        # the re-score's own rows (every sequence's kept entries, key pool rows in
+        # list order) gathered by a plain kernel from the same key replicas
+        cc, ci = p.cand_count.cpu().numpy(), p.cand_idx.cpu().numpy()
+        rs_rows = np.concatenate([wl.key_row_start[b] + ci[wl.entry_start[b]:wl.entry_start[b] + cc[b]]
+                                  for b in range(wl.B)])
+        if len(rs_rows):
+            hbm["rescore_gather_GBs"] = round(measured_row_gather(
+                torch, stream, d.keys, rs_rows, wl.D * wl.keys.itemsize), 1)
+            hbm["rescore_gather"] = (f"{len(rs_rows)} kept {wl.D * wl.keys.itemsize}-byte key rows "
+                                     f"(the step's lists) per launch")
     burst = None
     if wl.T == 1:
         # the tau-burst trigger score on its own workload, beside the decode step
@@ -570,6 +602,12 @@ def main():
         if unit == "GB/s":   # against the ceilings measured in this run, too
             r["frac_of_measured_read"] = round(ach / hbm["read_GBs"], 4)
             r["frac_of_measured_copy"] = round(ach / hbm["copy_GBs"], 4)
+        return r
+
+    def rescore_roof(r):
+        """the re-score gathers key rows: also rate it against a gather of the same rows"""
+        if "rescore_gather_GBs" in hbm:
+            r["frac_of_measured_gather"] = round(r["achieved"] / hbm["rescore_gather_GBs"], 4)
         return r
 
     def gather_roof(r):
@@ -630,8 +668,8 @@ def main():
         "attended_rows_per_step": att_rows,
         "roofline": roofline,
         "roofline_attend": roof_att,
-        "roofline_rescore": roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s",
-                                 read_traffic("rescore", args.workload, "rescore.hip")),
+        "roofline_rescore": rescore_roof(roof("hbm", rescore_bytes, t_rescore, HBM_PEAK_GBS, "GB/s",
+                                              read_traffic("rescore", args.workload, "rescore.hip"))),
         "roofline_union3": None if wl.T != 1 else roof(
             "hbm", union3_bytes, t_union3f, HBM_PEAK_GBS, "GB/s",
             read_traffic("score_union", args.workload, "score.hip")),

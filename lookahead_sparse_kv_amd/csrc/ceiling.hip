@@ -63,8 +63,11 @@ __global__ __launch_bounds__(kThreads) void k_copy(const u32x4* __restrict__ src
     }
 }
 
-// Rows of row16 16-byte words; a wave reads whole rows (64 words per instruction
-// across its lanes), kUnroll rows in flight, rows idx[r] for r in its share.
+// Rows of row16 16-byte words, rows idx[r] for r in the wave's share, kUnroll
+// row groups in flight.  A row of at least 64 words is read by the whole wave
+// (64 words per instruction); a shorter one (64 a multiple of row16) shares an
+// instruction with 64 / row16 - 1 others, lane l reading word l % row16 of row
+// l / row16 of the group.
 __global__ __launch_bounds__(kThreads) void k_gather(const u32x4* __restrict__ src,
                                                      const int32_t* __restrict__ idx,
                                                      int64_t nrows, int row16,
@@ -72,17 +75,21 @@ __global__ __launch_bounds__(kThreads) void k_gather(const u32x4* __restrict__ s
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+    const int rpi = row16 < 64 ? 64 / row16 : 1;          // rows per instruction
+    const int sub = row16 < 64 ? lane / row16 : 0;
+    const int c0 = row16 < 64 ? lane % row16 : lane;
     uint32_t acc = 0;
-    for (int64_t r0 = wave * kUnroll; r0 < nrows; r0 += nwaves * kUnroll) {
+    for (int64_t r0 = wave * kUnroll * rpi; r0 < nrows; r0 += nwaves * kUnroll * rpi) {
         int32_t rr[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) rr[u] = idx[min(r0 + u, nrows - 1)];
-        for (int c = lane; c < row16; c += 64) {
+        for (int u = 0; u < kUnroll; ++u) rr[u] = idx[min(r0 + u * rpi + sub, nrows - 1)];
+        for (int c = c0; c < row16; c += 64) {
             u32x4 v[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u)
-                v[u] = r0 + u < nrows ? __builtin_nontemporal_load(src + (int64_t)rr[u] * row16 + c)
-                                      : u32x4{0, 0, 0, 0};
+                v[u] = r0 + u * rpi + sub < nrows
+                           ? __builtin_nontemporal_load(src + (int64_t)rr[u] * row16 + c)
+                           : u32x4{0, 0, 0, 0};
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) acc ^= fold(v[u]);
         }
@@ -113,10 +120,12 @@ extern "C" int ceiling_copy(const void* src, void* dst, int64_t bytes, int grid,
     return status(hipGetLastError());
 }
 
-// Rows of row_bytes at src + idx[r] * row_bytes, r < nrows (indices must be valid rows).
+// Rows of row_bytes at src + idx[r] * row_bytes, r < nrows (indices must be valid
+// rows); below 1 KiB, row_bytes must divide 1 KiB.
 extern "C" int ceiling_gather(const void* src, const int32_t* idx, int64_t nrows,
                               int64_t row_bytes, int grid, uint32_t* sink, void* stream) {
-    if (!src || !idx || !sink || nrows <= 0 || row_bytes <= 0 || row_bytes % 16 || grid <= 0)
+    if (!src || !idx || !sink || nrows <= 0 || row_bytes <= 0 || row_bytes % 16 || grid <= 0 ||
+        (row_bytes < 1024 && 1024 % row_bytes))
         return -1;
     hipLaunchKernelGGL(k_gather, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
                        (const u32x4*)src, idx, nrows, (int)(row_bytes / 16), sink);
