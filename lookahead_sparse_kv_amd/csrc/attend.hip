@@ -21,7 +21,8 @@
 //   3. O[:, dims_u] += P C[:, dims_u]: value wave u owns Dl/4 latent dims of
 //      all 64 query rows; C^T operands come from transposing LDS reads.
 // Steps 2 and 3 of consecutive chunks overlap (a score wave and a value wave
-// share each SIMD).  Rows are split across workgroups when B * T * Hq is
+// share each SIMD), and the copies of step 1 are spread among the products of
+// step 2.  Rows are split across workgroups when B * T * Hq is
 // small; a combine kernel merges the splits by their log-sum-exp.
 #include "common.hpp"
 
@@ -211,28 +212,28 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     // Chunks past the split's last are issued too, with an empty buffer range
     // (the hardware's range check then reads no memory), so every step issues
     // the same number of copies and the waits are branch-free.
-    auto issue_chunk = [&](int c) {
+    // Copy m (0 <= m < CPW, a compile-time value) of chunk c.
+    auto issue_copy = [&](int c, int m) {
         bf16* slot = ring0 + (c % NB) * (kChunk * Dl);
         const int range = c < nchunks ? Dl * 2 : 0;
         const int cl = c & 63;
+        const int i = m / RPI, s2 = m % RPI;
+        const int sub = lane / SL;                         // row of this lane in the instruction
+        const int rbase = 8 * wave + RPI * i;
+        const uint32_t lo = __builtin_amdgcn_readlane(raddr_lo[m], cl);
+        const uint32_t hi = __builtin_amdgcn_readlane(raddr_hi[m], cl);
+        void* row = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(row, (short)0, range, kBufferWord3);
+        if (RPI == 1 || sub == s2)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void*)(slot + rbase * Dl), 16,
+                (uint32_t)(16 * ((lane % SL) ^ slot_swz(rbase + s2))), 0, 0,
+                NT ? kAttNonTemporal : 0);
+    };
+    auto issue_chunk = [&](int c) {
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int sub = lane / SL;                     // row of this lane in the instruction
-            const int rbase = 8 * wave + RPI * i;
-#pragma unroll
-            for (int s2 = 0; s2 < RPI; ++s2) {
-                const uint32_t lo = __builtin_amdgcn_readlane(raddr_lo[RPI * i + s2], cl);
-                const uint32_t hi = __builtin_amdgcn_readlane(raddr_hi[RPI * i + s2], cl);
-                void* row = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-                const __amdgpu_buffer_rsrc_t rsrc =
-                    __builtin_amdgcn_make_buffer_rsrc(row, (short)0, range, kBufferWord3);
-                if (RPI == 1 || sub == s2)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rsrc, (__attribute__((address_space(3))) void*)(slot + rbase * Dl), 16,
-                        (uint32_t)(16 * ((lane % SL) ^ slot_swz(rbase + s2))), 0, 0,
-                        NT ? kAttNonTemporal : 0);
-            }
-        }
+        for (int m = 0; m < CPW; ++m) issue_copy(c, m);
     };
 
     // Score wave state: running max (base 2) of query row 16w + n16 (the same in
@@ -242,7 +243,10 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
 
     // Score wave w, chunk c: S^T tiles (chunk rows 16rt .., query rows 16w ..)
     // over the full latent depth, then P against the running max into
-    // pbuf[c & 1], and this wave's rescale flag into flags[c & 1][w].
+    // pbuf[c & 1], and this wave's rescale flag into flags[c & 1][w].  The copies
+    // of chunk c + NB - 2 are issued among the products, one every NSTEP / CPW
+    // steps: issued together after a barrier, the four score waves' copies
+    // queue at the CU's address unit for about a fifth of a chunk's time.
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
     auto score = [&](int c) {
         const int r0 = rs + c * kChunk;
@@ -272,10 +276,13 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             bf16x8 kb[KW];
 #pragma unroll
             for (int i = 0; i < KW; ++i) kb[i] = *kaddr(i);
+            constexpr int CSTEP = NSTEP / CPW;              // product steps per copy
+            static_assert(CSTEP * CPW == NSTEP, "copies spread over the products");
 #pragma unroll
             for (int i = 0; i < NSTEP; ++i) {
                 acc4[i & 3] = mfma16(kb[i % KW], qf[i >> 1], acc4[i & 3]);
                 if (i + KW < NSTEP) kb[i % KW] = *kaddr(i + KW);
+                if (i % CSTEP == CSTEP - 1) issue_copy(c + NB - 2, i / CSTEP);
             }
             sacc[0] = acc4[0] + acc4[2];
             sacc[1] = acc4[1] + acc4[3];
@@ -446,20 +453,21 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         // copies, so the counted waits below are exact.  The value
         // waves never issue a copy, so their transposing LDS reads never wait for
         // one.
+        // chunks 0 .. NB-3 now; score(c) issues chunk c + NB - 2 (and where no
+        // score runs, the chunk is issued on its own: every step issues CPW copies)
 #pragma unroll
-        for (int c = 0; c < NB - 1; ++c) issue_chunk(c);
-        wait_vmcnt<(NB - 2) * CPW>();       // chunk 0 staged (and Q, which is older)
+        for (int c = 0; c < NB - 2; ++c) issue_chunk(c);
+        wait_vmcnt<(NB - 3) * CPW>();       // chunk 0 staged (and Q, which is older)
         lds_barrier();                                          // X_{-1}: chunk 0 staged
         if (!q_ok) {
 #pragma unroll
             for (int kk = 0; kk < KDT; ++kk) qf[kk] = zero8();
         }
-        if (nchunks > 0) score(0);
+        if (nchunks > 0) score(0); else issue_chunk(NB - 2);
         for (int c = 0; c < nchunks; ++c) {
             wait_vmcnt<(NB - 3) * CPW>();   // chunk c+1 staged (chunks up to c+NB-2 issued)
             lds_barrier();                                      // X_c
-            issue_chunk(c + NB - 1);
-            if (c + 1 < nchunks) score(c + 1);
+            if (c + 1 < nchunks) score(c + 1); else issue_chunk(c + NB - 1);
         }
         wait_vmcnt<0>();                    // no copy lands after the loop
         // the row sum of query row 16w + n16 and its running max, for the value waves
