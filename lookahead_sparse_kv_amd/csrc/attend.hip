@@ -248,6 +248,8 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     // steps: issued together after a barrier, the four score waves' copies
     // queue at the CU's address unit for about a fifth of a chunk's time.
     typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     auto score = [&](int c) {
         const int r0 = rs + c * kChunk;
         const bf16* sl = ring0 + (c % NB) * (kChunk * Dl);
@@ -293,14 +295,20 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         const bool full = r0 + kChunk <= re;
         float x[2][4];
         bool over = false;
+        float cmax;                                 // this lane's largest logit of the chunk
         if (full) {
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    x[rt][v] = sacc[rt][v] * scale_log2;
-                    over = over || x[rt][v] > m_ref + kRescaleSlack;
-                }
+            // Rounding is monotone, so the largest scaled logit is the scaled
+            // largest product (smallest, for a negative scale): one product
+            // instead of eight before the compare.
+            float hi;
+            if (scale_log2 >= 0.0f)
+                hi = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                           fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+            else
+                hi = fminf(fminf(fminf(sacc[0][0], sacc[0][1]), fminf(sacc[0][2], sacc[0][3])),
+                           fminf(fminf(sacc[1][0], sacc[1][1]), fminf(sacc[1][2], sacc[1][3])));
+            cmax = hi * scale_log2;
+            over = cmax > m_ref + kRescaleSlack;
         } else {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
@@ -310,6 +318,8 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
                     x[rt][v] = valid ? sacc[rt][v] * scale_log2 : -INFINITY;
                     over = over || x[rt][v] > m_ref + kRescaleSlack;
                 }
+            cmax = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
         }
         // Lazy rescale: the running max stands unless some logit of the chunk
         // exceeds it by more than kRescaleSlack (always on the first chunk, as
@@ -317,8 +327,7 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
         // met across the four lanes of each row, and the factors published.
         int grew = 0;
         if (__ballot(over) != 0) {
-            float cm = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                             fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+            float cm = cmax;
             cm = fmaxf(cm, __shfl_xor(cm, 16));
             cm = fmaxf(cm, __shfl_xor(cm, 32));
             const bool grow = cm > m_ref + kRescaleSlack;
@@ -329,18 +338,38 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
             grew = __ballot(grow) != 0 ? 1 : 0;
         }
         bf16* pb = pbuf + (c & 1) * (kMQ * PROW) + (16 * wave + n16) * PROW + 4 * g;
+        if (full) {
+            // p = 2^(scale_log2 s - m_ref) with one rounding, converted two at a
+            // time; the row sum adds the rounded pairs (bf16 times 1 is exact)
+            const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            bf16x4 p4;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                // after the rescale step m_ref is finite whenever the chunk has a row
-                const bf16 p = (bf16)(full || x[rt][v] != -INFINITY
-                                          ? __builtin_amdgcn_exp2f(x[rt][v] - m_ref) : 0.0f);
-                p4[v] = p;
-                l_part += (float)p;                 // the sums use the rounded P that P C uses
+            for (int rt = 0; rt < 2; ++rt) {
+                f32x2 e01, e23;
+                e01[0] = __builtin_amdgcn_exp2f(fmaf(sacc[rt][0], scale_log2, -m_ref));
+                e01[1] = __builtin_amdgcn_exp2f(fmaf(sacc[rt][1], scale_log2, -m_ref));
+                e23[0] = __builtin_amdgcn_exp2f(fmaf(sacc[rt][2], scale_log2, -m_ref));
+                e23[1] = __builtin_amdgcn_exp2f(fmaf(sacc[rt][3], scale_log2, -m_ref));
+                const bf16x2 p01 = __builtin_convertvector(e01, bf16x2);
+                const bf16x2 p23 = __builtin_convertvector(e23, bf16x2);
+                l_part = __builtin_amdgcn_fdot2_f32_bf16(p01, ones, l_part, false);
+                l_part = __builtin_amdgcn_fdot2_f32_bf16(p23, ones, l_part, false);
+                const bf16x4 p4 = {p01[0], p01[1], p23[0], p23[1]};
+                *reinterpret_cast<bf16x4*>(pb + 16 * rt) = p4;
             }
-            *reinterpret_cast<bf16x4*>(pb + 16 * rt) = p4;
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                bf16x4 p4;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    // after the rescale step m_ref is finite whenever the chunk has a row
+                    const bf16 p = (bf16)(x[rt][v] != -INFINITY
+                                              ? __builtin_amdgcn_exp2f(x[rt][v] - m_ref) : 0.0f);
+                    p4[v] = p;
+                    l_part += (float)p;             // the sums use the rounded P that P C uses
+                }
+                *reinterpret_cast<bf16x4*>(pb + 16 * rt) = p4;
+            }
         }
         if (lane == 0) flags[4 * (c & 1) + wave] = grew;
     };
