@@ -335,6 +335,25 @@ def test_attend_running_max_moves(ref, growth):
     check_attention(o, orf, l, lr)
 
 
+@pytest.mark.parametrize("scale_mul", [-3.0, -40.0, 0.0, 8.0])
+def test_attend_scale_sign(ref, scale_mul):
+    """Negative, zero and large softmax scales on the matrix-core path (full and
+    partial chunks, row splits, HCA rows): the slack test of a full chunk takes
+    the largest raw product of a lane for a positive scale and the smallest for
+    a negative one (at -40 the logits span hundreds of powers of two, so a
+    running maximum that missed a growth would overflow the probabilities), and
+    a zero scale gives every attended row the same weight."""
+    wl = inputs.random_small(733, 2, 1, 4, 32, [2500, 700], k=1024, Hq=64, Dl=512,
+                             hca_lens=[300, 45])
+    rng = np.random.default_rng(7)
+    idx, cnt = _random_indices(rng, wl.seq_len, wl.k, [1024, 333])
+    scale = wl.scale * scale_mul
+    announce(f"attend scale {scale_mul} x 1/sqrt(Dl)")
+    o, l = _attend_gpu(wl, idx, cnt, scale=scale)
+    orf, lr = _attend_ref(ref, wl, idx, cnt, scale=scale)
+    check_attention(o, orf, l, lr)
+
+
 def test_attend_all_selected_equals_dense(ref):
     """Every entry kept, k >= S, no HCA: sparse attention is dense attention (torch, fp64)."""
     S, Hq, Dl = 700, 64, 512
