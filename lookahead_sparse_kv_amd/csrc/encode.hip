@@ -275,6 +275,7 @@ __global__ __launch_bounds__(NG * WPG * kWave) void k_encode_stream(EncGemm g) {
     const int t = wv * kWave + lane;
     const int r0 = (int)((int64_t)g.N * blockIdx.x / gridDim.x);
     const int r1 = (int)((int64_t)g.N * (blockIdx.x + 1) / gridDim.x);
+    if (r1 <= r0) return;                        // no rows (the host keeps G <= N)
     // Buffer loads with the row's byte range: chunks past the row's end read
     // zeros, so the products below need no branch (a branch would let the
     // compiler sink the first weight load behind the others and wait for all).
