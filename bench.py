@@ -460,19 +460,27 @@ def main():
         att_topk = int(np.minimum(p.topk_count.cpu().numpy(), wl.k).sum())
         att_hca = int(np.minimum(wl.hca_count, wl.max_hca).sum()) if wl.hca is not None else 0
         att_rows = att_topk + att_hca
-        if args.warmup:
-            capture(torch, stream, [lambda i=i: p.step(i) for i in range(args.warmup)]).replay()
-        timed = capture(torch, stream,
-                        [lambda i=i: p.step((args.warmup + i) % nrot) for i in range(args.steps)])
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        timed.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        step_s = e0.elapsed_time(e1) * 1e-3 / args.steps
-        del timed
+        # The step runs on one stream.  Beside it, the same steps with the
+        # attention's HCA phase forked onto a second stream after the score (it
+        # needs no top-k list) and joined before the selected phase.
+        side = torch.cuda.Stream()   # default priority
+        step_s_by = {}
+        for mode, sd in (("one_stream", None), ("two_stream", side)):
+            if args.warmup:
+                capture(torch, stream,
+                        [lambda i=i: p.step(i, stream, sd) for i in range(args.warmup)]).replay()
+            timed = capture(torch, stream, [lambda i=i: p.step((args.warmup + i) % nrot, stream, sd)
+                                            for i in range(args.steps)])
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            timed.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            step_s_by[mode] = e0.elapsed_time(e1) * 1e-3 / args.steps
+            del timed
+        step_s = step_s_by["one_stream"]
 
         # per-kernel launch durations: graphs of R back-to-back launches of one call
         def reps_for(est_s):
@@ -496,6 +504,13 @@ def main():
         r = reps_for(step_s / 4)
         t_attend = timed_graph(torch, stream, capture(
             torch, stream, [lambda i=i: p.attend(i) for i in range(r)]), r)
+        if wl.hca is not None:
+            t_att_hca = timed_graph(torch, stream, capture(
+                torch, stream, [lambda i=i: p.attend_hca(i) for i in range(r)]), r)
+            t_att_sel = timed_graph(torch, stream, capture(
+                torch, stream, [lambda i=i: p.attend_selected(i) for i in range(r)]), r)
+        else:
+            t_att_hca, t_att_sel = 0.0, t_attend
         # per-step native tiered selection on the current candidates: re-score + top-k
         r = reps_for(1e-5)
         t_rescore = timed_graph(torch, stream, capture(
@@ -638,6 +653,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step_two_stream": round(step_s_by["two_stream"] * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -654,6 +670,8 @@ def main():
                        "one_element_add_floor": round(t_floor * 1e6, 2),
                        "topk": round(t_topk * 1e6, 2),
                        "sparse_attend": round(t_attend * 1e6, 2),
+                       "sparse_attend_hca": round(t_att_hca * 1e6, 2),
+                       "sparse_attend_selected": round(t_att_sel * 1e6, 2),
                        "index_rescore": round(t_rescore * 1e6, 2),
                        "topk_native": round(t_topk_native * 1e6, 2),
                        "index_score_union3": round(t_union3 * 1e6, 2),

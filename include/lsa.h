@@ -26,7 +26,8 @@
  *   lsa_sparse_attend   -- the final core attention over the chosen entries
  *                          plus every heavily compressed (HCA, 128:1) entry,
  *                          which the design always keeps (opening paragraph of
- *                          section 2.1).
+ *                          section 2.1).  lsa_sparse_attend_hca and
+ *                          lsa_sparse_attend_selected split it in two phases.
  * The output of each call is an input of the next.
  *
  * Conventions shared by every call
@@ -300,6 +301,38 @@ int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int Dl,
                       const void* hca, const int64_t* hca_row_start, const int32_t* hca_count,
                       int64_t max_hca, float scale, void* out, float* lse, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* The same attention in two phases (section 2.1: the HCA entries are kept for
+ * every query, whatever the selection, so their part of the softmax needs no
+ * top-k list).  Softmax over a union of row sets is the log-sum-exp merge of
+ * per-set partials, so the phases give the output of lsa_sparse_attend, bit
+ * for bit, on the same arguments:
+ *   lsa_sparse_attend_hca       partials over the HCA rows into `workspace`.
+ *                               It reads neither the top-k list nor its
+ *                               counts, so it may run while they are produced
+ *                               (e.g. on a second stream beside lsa_topk).
+ *   lsa_sparse_attend_selected  the top-k rows and the merge of all partials
+ *                               into out/lse.  It takes every argument of
+ *                               lsa_sparse_attend.
+ * The selected phase must run after the HCA phase has completed, on the same
+ * workspace and the same qa, dtype, B, T, Hq, Dl, k, hca, hca_row_start,
+ * hca_count, max_hca and scale; the caller orders the two (one stream, or an
+ * event between two streams).  The workspace is sized as for lsa_sparse_attend.
+ * When that size is 0 or the shape takes the vector path, the HCA phase
+ * enqueues nothing and the selected phase computes everything.
+ * hca must not be NULL in lsa_sparse_attend_hca (INVALID_ARG).
+ * Errors: as lsa_sparse_attend. */
+int lsa_sparse_attend_hca(const void* qa, int dtype, int B, int T, int Hq, int Dl, int k,
+                          const void* hca, const int64_t* hca_row_start,
+                          const int32_t* hca_count, int64_t max_hca, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+int lsa_sparse_attend_selected(const void* qa, int dtype, int B, int T, int Hq, int Dl,
+                               const void* latent, const int64_t* latent_row_start,
+                               const int32_t* topk_idx, const int32_t* topk_count, int k,
+                               const void* hca, const int64_t* hca_row_start,
+                               const int32_t* hca_count, int64_t max_hca, float scale, void* out,
+                               float* lse, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Workspace bytes needed by op (LSA_OP_*) for the given host-side sizes;
  * arguments an op does not use are ignored.  Returns 0 for an unknown op. */

@@ -29,7 +29,7 @@ LSA_OP_ATTEND = 3
 
 EXPORTED = ["lsa_query_encode", "lsa_index_score", "lsa_index_score_union", "lsa_index_rescore",
             "lsa_select_compact", "lsa_select_compact_noalloc", "lsa_topk", "lsa_fetch_rows",
-            "lsa_sparse_attend",
+            "lsa_sparse_attend", "lsa_sparse_attend_hca", "lsa_sparse_attend_selected",
             "lsa_workspace_bytes", "lsa_status_string", "lsa_last_error", "lsa_version"]
 
 
@@ -62,6 +62,8 @@ def load_library(path: str = LIB_PATH):
     lib.lsa_fetch_rows.argtypes = [P, L, P, P, P, P, I, L, P, P, P]
     lib.lsa_query_encode.argtypes = [P, I, I, I, I, I, P, P, P, P, P, P, P]
     lib.lsa_sparse_attend.argtypes = [P, I, I, I, I, I, P, P, P, P, I, P, P, P, L, F, P, P, P, Z, P]
+    lib.lsa_sparse_attend_selected.argtypes = lib.lsa_sparse_attend.argtypes
+    lib.lsa_sparse_attend_hca.argtypes = [P, I, I, I, I, I, I, P, P, P, L, F, P, Z, P]
     lib.lsa_workspace_bytes.argtypes = [I, I, I, I, I, L, I, L]
     lib.lsa_workspace_bytes.restype = Z
     lib.lsa_status_string.argtypes = [I]
@@ -73,7 +75,7 @@ def load_library(path: str = LIB_PATH):
     for name in ("lsa_index_score", "lsa_index_rescore", "lsa_select_compact",
                  "lsa_select_compact_noalloc", "lsa_topk",
                  "lsa_fetch_rows", "lsa_query_encode",
-                 "lsa_sparse_attend"):
+                 "lsa_sparse_attend", "lsa_sparse_attend_hca", "lsa_sparse_attend_selected"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -330,7 +332,8 @@ def lsa_fetch_rows(src, src_row_start, idx, idx_start, count, max_count: int, ds
 
 def lsa_sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k: int, out,
                       hca=None, hca_row_start=None, hca_count=None, max_hca: int = 0,
-                      scale: Optional[float] = None, lse=None, workspace=None, stream=None):
+                      scale: Optional[float] = None, lse=None, workspace=None, stream=None,
+                      _entry: str = "lsa_sparse_attend"):
     lib = load_library()
     B, T, Hq, Dl = qa.shape
     _dev(qa, "qa")
@@ -343,10 +346,37 @@ def lsa_sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k: int
     if scale is None:
         scale = Dl ** -0.5
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    rc = lib.lsa_sparse_attend(_ptr(qa), _dtype_code(qa), B, T, Hq, Dl, _ptr(latent),
-                               _ptr(latent_row_start), _ptr(topk_idx), _ptr(topk_count), int(k),
-                               _ptr(hca), _ptr(hca_row_start), _ptr(hca_count), int(max_hca),
-                               float(scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
-                               _stream(stream))
-    _check("lsa_sparse_attend", rc)
+    rc = getattr(lib, _entry)(_ptr(qa), _dtype_code(qa), B, T, Hq, Dl, _ptr(latent),
+                              _ptr(latent_row_start), _ptr(topk_idx), _ptr(topk_count), int(k),
+                              _ptr(hca), _ptr(hca_row_start), _ptr(hca_count), int(max_hca),
+                              float(scale), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                              _stream(stream))
+    _check(_entry, rc)
     return out, lse
+
+
+def lsa_sparse_attend_hca(qa, k: int, hca, hca_row_start, hca_count, max_hca: int,
+                          scale: Optional[float] = None, workspace=None, stream=None):
+    """First phase of lsa_sparse_attend: the HCA rows' split partials into workspace."""
+    lib = load_library()
+    B, T, Hq, Dl = qa.shape
+    _dev(qa, "qa")
+    if hca is not None:
+        _dev(hca, "hca", qa.dtype)
+    if scale is None:
+        scale = Dl ** -0.5
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib.lsa_sparse_attend_hca(_ptr(qa), _dtype_code(qa), B, T, Hq, Dl, int(k), _ptr(hca),
+                                   _ptr(hca_row_start), _ptr(hca_count), int(max_hca),
+                                   float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("lsa_sparse_attend_hca", rc)
+
+
+def lsa_sparse_attend_selected(qa, latent, latent_row_start, topk_idx, topk_count, k: int, out,
+                               hca=None, hca_row_start=None, hca_count=None, max_hca: int = 0,
+                               scale: Optional[float] = None, lse=None, workspace=None,
+                               stream=None):
+    """Second phase: the top-k rows and the merge (after lsa_sparse_attend_hca)."""
+    return lsa_sparse_attend(qa, latent, latent_row_start, topk_idx, topk_count, k, out, hca,
+                             hca_row_start, hca_count, max_hca, scale, lse, workspace, stream,
+                             _entry="lsa_sparse_attend_selected")

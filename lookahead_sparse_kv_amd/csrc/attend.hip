@@ -33,6 +33,10 @@ namespace lsa {
 #define LSA_ATT_WG_TARGET 256
 #endif
 constexpr int kAttWGTarget = LSA_ATT_WG_TARGET;
+#ifndef LSA_ATT_TOP_ROWS
+#define LSA_ATT_TOP_ROWS 0
+#endif
+constexpr int kAttTopRows = LSA_ATT_TOP_ROWS;   // rows per top-k split; 0 = as the HCA splits
 // cache-policy operand of the row copies when every row is read by one workgroup
 // only (one query group): nontemporal, as the rows are streamed once
 constexpr int kAttNonTemporal = 2;
@@ -119,8 +123,9 @@ __device__ __forceinline__ float group_sum(float x) {
 // share a SIMD, so one's matrix products overlap the other's LDS traffic.
 template <int Dl, int NB, bool NT>
 __global__ __launch_bounds__(512, 1) void k_attend_mfma(
-    int n_items, int QG, int nsplit, int rows_per_split, int M, int k,
-    const int32_t* __restrict__ topk_idx, const bf16* __restrict__ qa,
+    int n_items, int QG, int nsplit, int split0, int nloc, int nts, int rps_top,
+    int rows_per_split, int M, int k, const int32_t* __restrict__ topk_idx,
+    const bf16* __restrict__ qa,
     const int32_t* __restrict__ topk_count, const int32_t* __restrict__ hca_count,
     const int64_t* __restrict__ latent_row_start, const int64_t* __restrict__ hca_row_start,
     int64_t max_hca, const bf16* __restrict__ latent, const bf16* __restrict__ hca,
@@ -165,8 +170,8 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     const int item = active ? item_raw : 0;
     const int tq = item / QG;
     const int qg = item - tq * QG;
-    const int b = tq / nsplit;
-    const int split = tq - b * nsplit;
+    const int b = tq / nloc;                    // this launch covers splits split0 .. +nloc-1
+    const int split = split0 + (tq - b * nloc);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -176,7 +181,6 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     const bool vwave = wave >= NS;
     const int u = wave - NS;                    // value wave: dims DPW*u ..
 
-    const int rs = split * rows_per_split;
     const int32_t* idx = topk_idx + (int64_t)b * k;
     const int64_t qrow0 = (int64_t)b * M + (int64_t)qg * kMQ;   // first query row of the group
     const int mq = min(kMQ, M - qg * kMQ);                        // valid query rows
@@ -187,10 +191,19 @@ __global__ __launch_bounds__(512, 1) void k_attend_mfma(
     const int hca_cnt = hca_count[b];
     const int64_t lrs = latent_row_start[b];
     const int64_t hrs = hca_row_start[b];
-    const int ntop = min(topk_cnt, k);
+    // Rows of the sequence: its top-k rows, then its HCA rows.  With nts = 0 the
+    // splits take consecutive runs of rows_per_split of that list.  With nts > 0
+    // splits 0 .. nts-1 take runs of rps_top top-k rows and the rest runs of
+    // rows_per_split HCA rows, so a launch of HCA splits only never reads the
+    // top-k list or its counts (it runs with ntop = 0: every row is an HCA row).
+    const bool hsplit = nts > 0 && split >= nts;
+    const int ntop = hsplit ? 0 : min(topk_cnt, k);
     const int nh = (int)min((int64_t)hca_cnt, max_hca);   // max_hca = 0 without a pool
     const int n = ntop + nh;
-    const int re = min(n, rs + rows_per_split);
+    const int rs = nts == 0 ? split * rows_per_split
+                 : hsplit   ? (split - nts) * rows_per_split
+                            : split * rps_top;
+    const int re = nts > 0 && !hsplit ? min(ntop, rs + rps_top) : min(n, rs + rows_per_split);
     const int nchunks = (active && re > rs) ? (re - rs + kChunk - 1) / kChunk : 0;
 
     // Score wave w stages rows 8w .. 8w+7 of every chunk: lane c holds the 64-bit
@@ -822,14 +835,19 @@ __global__ __launch_bounds__(256) void k_attend_vector(
     if (threadIdx.x == 0 && lse) lse[bt * Hq + h] = L > 0.0f ? M + logf(L) : -INFINITY;
 }
 
-// Split heuristic shared by the launch and the workspace query: groups of kMQ
+// Split heuristic shared by the launches and the workspace query: groups of kMQ
 // query rows, then enough row splits to give ~kAttWGTarget workgroups, keeping
-// at least two row chunks per split.
+// at least two row chunks per split.  When the rows are split and an HCA pool is
+// given, no split mixes top-k rows and HCA rows: splits 0 .. nts-1 take the
+// top-k list (rps_top rows each, at most k in all) and the rest the HCA rows,
+// so the HCA splits can run before the top-k list exists.
 struct AttendPlan {
     int QG;
-    int nsplit;
-    int rows_per_split;
-    int n_items;
+    int nsplit;          // splits per (sequence, query group)
+    int rows_per_split;  // rows per split (per HCA split when nts > 0)
+    int nts;             // top-k splits; 0 = splits over the joined row list
+    int rps_top;         // rows per top-k split (nts > 0)
+    int n_items;         // B * QG * nsplit
 };
 
 static AttendPlan attend_plan(int B, int T, int Hq, int k, int64_t max_hca) {
@@ -847,7 +865,15 @@ static AttendPlan attend_plan(int B, int T, int Hq, int k, int64_t max_hca) {
     if (rps > kMaxSplitRows) rps = kMaxSplitRows;
     ns = (rows + rps - 1) / rps;
     if (ns < 1) ns = 1;
-    return AttendPlan{QG, (int)ns, (int)rps, (int)(units * ns)};
+    if (ns == 1 || max_hca <= 0)
+        return AttendPlan{QG, (int)ns, (int)rps, 0, 0, (int)(units * ns)};
+    int64_t rtop = kAttTopRows > 0 ? kAttTopRows : rps;
+    rtop = (rtop + kChunk - 1) / kChunk * kChunk;
+    if (rtop > kMaxSplitRows) rtop = kMaxSplitRows;
+    const int64_t nts = ((int64_t)k + rtop - 1) / rtop;
+    const int64_t nhs = (max_hca + rps - 1) / rps;
+    return AttendPlan{QG, (int)(nts + nhs), (int)rps, (int)nts, (int)rtop,
+                      (int)(units * (nts + nhs))};
 }
 
 static bool attend_mfma_shape(int dtype, int Hq, int Dl) {
@@ -867,48 +893,88 @@ size_t lsa_attend_workspace(int dtype, int B, int T, int Hq, int Dl, int k, int6
     return n * Dl * sizeof(bf16) + n * sizeof(float);
 }
 
-extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int Dl,
-                                 const void* latent, const int64_t* latent_row_start,
-                                 const int32_t* topk_idx, const int32_t* topk_count, int k,
-                                 const void* hca, const int64_t* hca_row_start,
-                                 const int32_t* hca_count, int64_t max_hca, float scale, void* out,
-                                 float* lse, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+// phase: kAttAll = every split and the merge; kAttHca = the HCA splits only
+// (partials into the workspace; nothing when the plan has none);
+// kAttSelected = the remaining splits and the merge.
+enum { kAttAll = 0, kAttHca = 1, kAttSelected = 2 };
+
+static int attend_impl(const char* name, int phase, const void* qa, int dtype, int B, int T,
+                       int Hq, int Dl, const void* latent, const int64_t* latent_row_start,
+                       const int32_t* topk_idx, const int32_t* topk_count, int k, const void* hca,
+                       const int64_t* hca_row_start, const int32_t* hca_count, int64_t max_hca,
+                       float scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     clear_error();
-    if (!qa || !latent || !latent_row_start || !topk_idx || !topk_count || !out)
-        return fail(LSA_ERR_INVALID_ARG, "lsa_sparse_attend: a required pointer is NULL");
+    if (!qa || (phase != kAttHca && (!latent || !latent_row_start || !topk_idx || !topk_count ||
+                                     !out)))
+        return fail(LSA_ERR_INVALID_ARG, "%s: a required pointer is NULL", name);
+    if (phase == kAttHca && !hca)
+        return fail(LSA_ERR_INVALID_ARG, "%s: the HCA pool is NULL", name);
     if (hca && (!hca_row_start || !hca_count))
-        return fail(LSA_ERR_INVALID_ARG, "lsa_sparse_attend: hca given without row starts/counts");
+        return fail(LSA_ERR_INVALID_ARG, "%s: hca given without row starts/counts", name);
     if (B <= 0 || T <= 0 || Hq <= 0 || Dl <= 0 || k <= 0 || (hca && max_hca < 0))
-        return fail(LSA_ERR_INVALID_ARG, "lsa_sparse_attend: B=%d T=%d Hq=%d Dl=%d k=%d", B, T, Hq,
-                    Dl, k);
+        return fail(LSA_ERR_INVALID_ARG, "%s: B=%d T=%d Hq=%d Dl=%d k=%d", name, B, T, Hq, Dl, k);
     if (dtype != LSA_DTYPE_F32 && dtype != LSA_DTYPE_BF16)
-        return fail(LSA_ERR_INVALID_ARG, "lsa_sparse_attend: unknown dtype %d", dtype);
-    if (!aligned16(qa) || !aligned16(latent) || (hca && !aligned16(hca)))
-        return fail(LSA_ERR_INVALID_ARG, "lsa_sparse_attend: qa/latent/hca must be 16-byte aligned");
-    if (!(scale == scale)) return fail(LSA_ERR_INVALID_ARG, "lsa_sparse_attend: scale is NaN");
-    if (Dl > 1024) return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: Dl=%d > 1024", Dl);
+        return fail(LSA_ERR_INVALID_ARG, "%s: unknown dtype %d", name, dtype);
+    if (!aligned16(qa) || (latent && !aligned16(latent)) || (hca && !aligned16(hca)))
+        return fail(LSA_ERR_INVALID_ARG, "%s: qa/latent/hca must be 16-byte aligned", name);
+    if (!(scale == scale)) return fail(LSA_ERR_INVALID_ARG, "%s: scale is NaN", name);
+    if (Dl > 1024) return fail(LSA_ERR_UNSUPPORTED, "%s: Dl=%d > 1024", name, Dl);
     if (B > 65535 || T > 65535)
-        return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: B or T above 65535");
+        return fail(LSA_ERR_UNSUPPORTED, "%s: B or T above 65535", name);
     if ((int64_t)k + (hca ? max_hca : 0) > kMaxAttendRows)
-        return fail(LSA_ERR_UNSUPPORTED, "lsa_sparse_attend: k + max_hca above %lld rows",
+        return fail(LSA_ERR_UNSUPPORTED, "%s: k + max_hca above %lld rows", name,
                     (long long)kMaxAttendRows);
     const int64_t hmax = hca ? max_hca : 0;
     const size_t need = lsa_attend_workspace(dtype, B, T, Hq, Dl, k, hmax);
     if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(LSA_ERR_WORKSPACE, "lsa_sparse_attend: workspace %zu < %zu bytes",
-                    workspace_bytes, need);
+        return fail(LSA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", name, workspace_bytes,
+                    need);
     int cus = 0;
     int rc = check_device(&cus);
     if (rc != LSA_OK) return rc;
     hipStream_t st = (hipStream_t)stream;
+    const bool mfma = attend_mfma_shape(dtype, Hq, Dl);
+    if (phase == kAttHca) {
+        // Only a split plan has HCA splits of their own; otherwise the selected
+        // phase attends every row and this phase enqueues nothing.
+        if (!mfma) return LSA_OK;
+        const AttendPlan p = attend_plan(B, T, Hq, k, hmax);
+        if (p.nts == 0) return LSA_OK;
+        const size_t n = (size_t)B * p.nsplit * p.QG * kMQ;
+        bf16* part_o = (bf16*)workspace;
+        float* part_lse = (float*)(part_o + n * Dl);
+        const int nloc = p.nsplit - p.nts;
+        const int n_items = B * p.QG * nloc;
+        const unsigned grid = (unsigned)(8 * ((n_items + 7) / 8));
+        const float sl2 = scale * kLog2e;
+        const int M = T * Hq;
+        // Stand-ins for the top-k arguments: HCA splits read no top-k row, and
+        // with k = 1 the kernel's speculative index loads stay inside hca_count.
+#define LSA_ATT_H(dl, nt)                                                                      \
+    hipLaunchKernelGGL((k_attend_mfma<dl, kAttRing, nt>), dim3(grid), dim3(512), 0, st,         \
+                       n_items, p.QG, p.nsplit, p.nts, nloc, p.nts, p.rps_top, p.rows_per_split, \
+                       M, 1, hca_count, (const bf16*)qa, hca_count, hca_count, hca_row_start,   \
+                       hca_row_start, hmax, (const bf16*)hca, (const bf16*)hca, sl2,            \
+                       (bf16*)nullptr, (float*)nullptr, part_o, part_lse)
+        if (p.QG == 1) {
+            if (Dl == 512) LSA_ATT_H(512, true); else if (Dl == 256) LSA_ATT_H(256, true); else LSA_ATT_H(128, true);
+        } else {
+            if (Dl == 512) LSA_ATT_H(512, false); else if (Dl == 256) LSA_ATT_H(256, false); else LSA_ATT_H(128, false);
+        }
+#undef LSA_ATT_H
+        return launch_status("attend_mfma");
+    }
 
     if (attend_mfma_shape(dtype, Hq, Dl)) {
         const AttendPlan p = attend_plan(B, T, Hq, k, hmax);
         const size_t n = (size_t)B * p.nsplit * p.QG * kMQ;
         bf16* part_o = (bf16*)workspace;
         float* part_lse = p.nsplit > 1 ? (float*)(part_o + n * Dl) : nullptr;
-        const unsigned grid = (unsigned)(8 * ((p.n_items + 7) / 8));
+        // the selected phase runs the top-k splits only (the HCA splits ran before)
+        const int nloc = (phase == kAttSelected && p.nts > 0) ? p.nts : p.nsplit;
+        const int n_items = B * p.QG * nloc;
+        const unsigned grid = (unsigned)(8 * ((n_items + 7) / 8));
         const float sl2 = scale * kLog2e;
         const int M = T * Hq;
         // Without an HCA pool the kernel reads valid stand-ins and attends zero
@@ -918,7 +984,8 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
         const int32_t* hcnt_p = hca ? hca_count : topk_count;
 #define LSA_ATT(dl, nt)                                                                        \
     hipLaunchKernelGGL((k_attend_mfma<dl, kAttRing, nt>), dim3(grid), dim3(512), 0, st,         \
-                       p.n_items, p.QG, p.nsplit, p.rows_per_split, M, k, topk_idx,             \
+                       n_items, p.QG, p.nsplit, 0, nloc, p.nts, p.rps_top, p.rows_per_split,    \
+                       M, k, topk_idx,                                                          \
                        (const bf16*)qa, topk_count, hcnt_p, latent_row_start, hrs_p, hmax,      \
                        (const bf16*)latent, (const bf16*)hp, sl2, (bf16*)out, lse, part_o,      \
                        part_lse)
@@ -978,4 +1045,38 @@ extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq
 #undef LSA_ATTV_NPL
 #undef LSA_ATTV
     return launch_status("attend_vector");
+}
+
+extern "C" int lsa_sparse_attend(const void* qa, int dtype, int B, int T, int Hq, int Dl,
+                                 const void* latent, const int64_t* latent_row_start,
+                                 const int32_t* topk_idx, const int32_t* topk_count, int k,
+                                 const void* hca, const int64_t* hca_row_start,
+                                 const int32_t* hca_count, int64_t max_hca, float scale, void* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    return attend_impl("lsa_sparse_attend", kAttAll, qa, dtype, B, T, Hq, Dl, latent,
+                       latent_row_start, topk_idx, topk_count, k, hca, hca_row_start, hca_count,
+                       max_hca, scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" int lsa_sparse_attend_hca(const void* qa, int dtype, int B, int T, int Hq, int Dl,
+                                     int k, const void* hca, const int64_t* hca_row_start,
+                                     const int32_t* hca_count, int64_t max_hca, float scale,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+    return attend_impl("lsa_sparse_attend_hca", kAttHca, qa, dtype, B, T, Hq, Dl, nullptr,
+                       nullptr, nullptr, nullptr, k, hca, hca_row_start, hca_count, max_hca,
+                       scale, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" int lsa_sparse_attend_selected(const void* qa, int dtype, int B, int T, int Hq,
+                                          int Dl, const void* latent,
+                                          const int64_t* latent_row_start,
+                                          const int32_t* topk_idx, const int32_t* topk_count,
+                                          int k, const void* hca, const int64_t* hca_row_start,
+                                          const int32_t* hca_count, int64_t max_hca, float scale,
+                                          void* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream) {
+    return attend_impl("lsa_sparse_attend_selected", kAttSelected, qa, dtype, B, T, Hq, Dl,
+                       latent, latent_row_start, topk_idx, topk_count, k, hca, hca_row_start,
+                       hca_count, max_hca, scale, out, lse, workspace, workspace_bytes, stream);
 }

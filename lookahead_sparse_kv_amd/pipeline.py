@@ -171,8 +171,38 @@ class Pipeline:
                               max_hca=d.max_hca, scale=d.scale, lse=self.lse,
                               workspace=self.ws_attend, stream=stream)
 
-    def step(self, replica: int = 0, stream=None):
+    def attend_hca(self, replica: int = 0, stream=None):
+        d = self.d
+        r = replica % len(d.latent)
+        lsa.lsa_sparse_attend_hca(d.qa, d.k, d.hca[r], d.hca_row_start, d.hca_count, d.max_hca,
+                                  scale=d.scale, workspace=self.ws_attend, stream=stream)
+
+    def attend_selected(self, replica: int = 0, stream=None):
+        d = self.d
+        r = replica % len(d.latent)
+        lsa.lsa_sparse_attend_selected(d.qa, d.latent[r], d.latent_row_start, self.topk_idx,
+                                       self.topk_count, d.k, self.out, hca=d.hca[r],
+                                       hca_row_start=d.hca_row_start, hca_count=d.hca_count,
+                                       max_hca=d.max_hca, scale=d.scale, lse=self.lse,
+                                       workspace=self.ws_attend, stream=stream)
+
+    def step(self, replica: int = 0, stream=None, side=None):
+        """One decode step.  With a second stream `side`, the attention's HCA
+        phase (which needs no top-k list) runs there beside the gate and the
+        top-k, forked after the score and joined before the selected phase."""
         self.score(replica, stream)
-        self.select(stream)
-        self.topk(stream)
-        self.attend(replica, stream)
+        if side is None or self.d.hca is None:
+            self.select(stream)
+            self.topk(stream)
+            self.attend(replica, stream)
+            return
+        main = stream if stream is not None else torch.cuda.current_stream()
+        fork, join = torch.cuda.Event(), torch.cuda.Event()
+        fork.record(main)
+        side.wait_event(fork)
+        self.attend_hca(replica, side)
+        join.record(side)
+        self.select(main)
+        self.topk(main)
+        main.wait_event(join)
+        self.attend_selected(replica, main)
